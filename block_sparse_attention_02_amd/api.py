@@ -1,0 +1,267 @@
+"""Python binding of libh3attn (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU (PyTorch is
+used for device memory and streams), passes raw pointers to the C entry point
+of the same name in include/h3attn.h, and raises ``H3Error`` on a nonzero
+status. All computation happens in the HIP library; if the library has not
+been built, the first call raises ``RuntimeError`` rather than falling back
+to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3attn.so")
+
+H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE = 0, -1, -2, -3, -4
+H3_DTYPE_F32, H3_DTYPE_BF16 = 0, 1
+
+EXPORTS = (
+    "h3attn_version", "h3attn_status_string",
+    "attn_dense_tara_workspace", "attn_dense_tara",
+    "attn_router_plan", "attn_block_router_workspace", "attn_block_router",
+    "attn_block_sparse_workspace", "attn_block_sparse",
+    "partition_lse_merge",
+    "attn_dense_tara_via_workspace", "attn_dense_tara_via",
+)
+
+_vp, _i, _f, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+_SIGS = {
+    "h3attn_version": (_i, []),
+    "h3attn_status_string": (ctypes.c_char_p, [_i]),
+    "attn_dense_tara_workspace": (_sz, [_i, _i, _i, _i]),
+    "attn_dense_tara": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                             _f, _f, _f, _f, _f, _vp, _i, _vp, _vp, _sz, _vp]),
+    "attn_router_plan": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
+    "attn_block_router_workspace": (_sz, [_i, _i, _i, _i]),
+    "attn_block_router": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i,
+                               _vp, _sz, _vp]),
+    "attn_block_sparse_workspace": (_sz, [_i, _i, _i, _i]),
+    "attn_block_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f, _f,
+                               _i, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _sz, _vp]),
+    "partition_lse_merge": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _vp]),
+    "attn_dense_tara_via_workspace": (_sz, [_vp, _vp, _i, _i, _i, _i]),
+    "attn_dense_tara_via": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                 _f, _f, _f, _f, _f, _vp, _i, _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class H3Error(RuntimeError):
+    def __init__(self, func, status):
+        self.status = status
+        super().__init__(f"{func} failed with status {status} ({status_string(status)})")
+
+
+def lib():
+    """The loaded library (loaded once, with argument types declared)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().h3attn_status_string(status).decode()
+
+
+def _check(name, status):
+    if status != H3_OK:
+        raise H3Error(name, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return H3_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return H3_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _empty_like_out(q, o_dtype):
+    import torch
+    return torch.empty(q.shape, dtype=o_dtype, device=q.device)
+
+
+def _workspace(nbytes, device):
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def dense_tara_workspace_bytes(nk, heads, head_dim, dtype_code):
+    return int(lib().attn_dense_tara_workspace(nk, heads, head_dim, dtype_code))
+
+
+def attn_dense_tara(q, k, v, q_seg, q_t, k_seg, k_t, strength=2.0, window=0.20, falloff=0.25,
+                    cap=6.0, scale=None, o=None, o_dtype=None, lse=None, ws=None, stream=None):
+    """Dense TARA attention (attn_dense_tara). q [nq,H,d], k/v [nk,H,d] on the GPU.
+
+    Returns (o, lse) with lse [nq, H] float32 (natural log).
+    """
+    import torch
+    nq, H, D = q.shape
+    nk = k.shape[0]
+    dt = _dtype_code(q)
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((nq, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    need = dense_tara_workspace_bytes(nk, H, D, dt)
+    if ws is None:
+        ws = _workspace(need, q.device)
+    _contig(q, k, v, q_seg, q_t, k_seg, k_t, o, lse)
+    st = lib().attn_dense_tara(_ptr(q), _ptr(k), _ptr(v), dt, nq, nk, H, D,
+                               _ptr(q_seg), _ptr(q_t), _ptr(k_seg), _ptr(k_t),
+                               strength, window, falloff, cap, scale,
+                               _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_dense_tara", st)
+    return o, lse
+
+
+def router_plan(seg_host, protected_prefix_len, sparsity_ratio, block_size=64):
+    """Host-only routing plan: dict(nb, n_video, n_prot, k_sel)."""
+    seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+    outs = [ctypes.c_int(0) for _ in range(4)]
+    st = lib().attn_router_plan(_np_ptr(seg_host), len(seg_host), protected_prefix_len,
+                                block_size, float(sparsity_ratio),
+                                *[ctypes.byref(x) for x in outs])
+    _check("attn_router_plan", st)
+    nb, nv, npr, k = (x.value for x in outs)
+    return {"nb": nb, "n_video": nv, "n_prot": npr, "k_sel": k}
+
+
+def router_workspace_bytes(n, heads, head_dim, block_size=64):
+    return int(lib().attn_block_router_workspace(n, heads, head_dim, block_size))
+
+
+def attn_block_router(q, k, seg, protected_prefix_len, k_sel, n_prot, block_size=64,
+                      tiles=None, prot=None, ws=None, stream=None):
+    """Pooled router: returns (tiles int32 [H, nb, k_sel], prot int32 [n_prot])."""
+    import torch
+    n, H, D = q.shape
+    nb = (n + block_size - 1) // block_size
+    if tiles is None:
+        tiles = torch.empty((H, nb, k_sel), dtype=torch.int32, device=q.device)
+    if prot is None:
+        prot = torch.empty((n_prot,), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = _workspace(router_workspace_bytes(n, H, D, block_size), q.device)
+    _contig(q, k, seg, tiles, prot)
+    st = lib().attn_block_router(_ptr(q), _ptr(k), _dtype_code(q), n, H, D, _ptr(seg),
+                                 protected_prefix_len, block_size, k_sel,
+                                 _ptr(tiles) if k_sel > 0 else None,
+                                 _ptr(prot) if n_prot > 0 else None, n_prot,
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_block_router", st)
+    return tiles, prot
+
+
+def attn_block_sparse(q, k, v, seg, t, tiles, prot, strength=2.0, window=0.20, falloff=0.25,
+                      cap=6.0, scale=None, block_size=64, o=None, o_dtype=None, lse=None,
+                      ws=None, stream=None):
+    """Block-sparse attention over routed tiles: returns (o, lse)."""
+    import torch
+    n, H, D = q.shape
+    dt = _dtype_code(q)
+    k_sel = int(tiles.shape[-1]) if tiles is not None else 0
+    n_prot = int(prot.numel()) if prot is not None else 0
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if ws is None:
+        ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
+    _contig(q, k, v, seg, t, tiles, prot, o, lse)
+    st = lib().attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
+                                 strength, window, falloff, cap, scale, block_size,
+                                 _ptr(tiles) if k_sel > 0 else None, k_sel,
+                                 _ptr(prot) if n_prot > 0 else None, n_prot,
+                                 _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_block_sparse", st)
+    return o, lse
+
+
+def partition_lse_merge(o_acc, lse_acc, o_i, lse_i, log_w=0.0, log_w_rows=None, stream=None):
+    """In-place stable LSE merge of (o_i, lse_i) into (o_acc, lse_acc)."""
+    rows, H, D = o_acc.shape
+    _contig(o_acc, lse_acc, o_i, lse_i, log_w_rows)
+    st = lib().partition_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_i), _ptr(lse_i),
+                                   float(log_w), _ptr(log_w_rows), rows, H, D, _stream(stream))
+    _check("partition_lse_merge", st)
+    return o_acc, lse_acc
+
+
+def via_workspace_bytes(seg_host, t_host, heads, head_dim, dtype_code):
+    seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+    t_host = np.ascontiguousarray(t_host, dtype=np.float32)
+    return int(lib().attn_dense_tara_via_workspace(_np_ptr(seg_host), _np_ptr(t_host),
+                                                   len(seg_host), heads, head_dim, dtype_code))
+
+
+def attn_dense_tara_via(q, k, v, seg, t, seg_host, t_host, strength=2.0, window=0.20,
+                        falloff=0.25, cap=6.0, scale=None, o=None, o_dtype=None, lse=None,
+                        ws=None, stream=None):
+    """Dense TARA through the positive-partition decomposition: returns (o, lse)."""
+    import torch
+    n, H, D = q.shape
+    dt = _dtype_code(q)
+    seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+    t_host = np.ascontiguousarray(t_host, dtype=np.float32)
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if ws is None:
+        ws = _workspace(via_workspace_bytes(seg_host, t_host, H, D, dt), q.device)
+    _contig(q, k, v, seg, t, o, lse)
+    st = lib().attn_dense_tara_via(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
+                                   _np_ptr(seg_host), _np_ptr(t_host), strength, window,
+                                   falloff, cap, scale, _ptr(o), _dtype_code(o), _ptr(lse),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_dense_tara_via", st)
+    return o, lse

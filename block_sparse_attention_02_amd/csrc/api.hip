@@ -1,0 +1,404 @@
+// C entry points of libh3attn: argument checks, workspace layout, launch dispatch, and
+// the host-side plan of the positive-partition ("via") path.
+//
+// Every check runs before the first HIP call, so a rejected call never touches the
+// device. Kernels run on the caller's stream; nothing here synchronises.
+#include <cmath>
+#include <vector>
+
+#include "../../include/h3attn.h"
+#include "h3_internal.h"
+
+using namespace h3;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool finite(float x) { return std::isfinite(x); }
+
+int check_tara(float strength, float window, float falloff, float cap, float scale) {
+  if (!finite(strength) || !finite(window) || !finite(falloff) || !finite(cap) || !finite(scale))
+    return H3_EINVAL;
+  if (strength < 0.f || window < 0.f || cap < 0.f || !(falloff > 0.f) || !(scale > 0.f))
+    return H3_EINVAL;
+  return H3_OK;
+}
+
+bool dtype_ok(int dt) { return dt == H3_DTYPE_F32 || dt == H3_DTYPE_BF16; }
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+size_t vt_bytes(int nk, int heads, int head_dim) {
+  return (size_t)pad_keys(nk) * (size_t)heads * (size_t)head_dim * sizeof(uint16_t);
+}
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, int heads,
+                   const uint8_t* q_seg, const float* q_t, const uint8_t* k_seg,
+                   const float* k_t, float strength, float window, float falloff, float cap,
+                   float scale, void* o, int o_dtype, float* lse) {
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.vt = nullptr;
+  a.q_seg = q_seg; a.q_t = q_t; a.k_seg = k_seg; a.k_t = k_t;
+  a.o = o; a.lse = lse;
+  a.nq = nq; a.nk = nk; a.nkp = (int)pad_keys(nk); a.H = heads;
+  a.o_f32 = (o_dtype == H3_DTYPE_F32);
+  a.scale = scale;
+  a.strength = strength; a.window = window; a.inv_falloff = 1.f / falloff; a.cap = cap;
+  a.prot = nullptr; a.n_prot = 0; a.tiles = nullptr; a.k_sel = 0; a.nqb = 0;
+  return a;
+}
+
+// One attention launch over (queries, keys); the bf16 path first writes the
+// transposed v copy into `vt` unless `vt_ready` says it is already there.
+hipError_t run_attention(AttnArgs a, int dtype, int head_dim, bool sparse, bool penalty,
+                         uint16_t* vt, bool vt_ready, hipStream_t s) {
+  if (dtype == H3_DTYPE_BF16) {
+    if (!vt_ready) {
+      hipError_t e = launch_vt_transpose((const uint16_t*)a.v, vt, a.nk, a.H, head_dim, s);
+      if (e != hipSuccess) return e;
+    }
+    a.vt = vt;
+    return launch_attn_bf16(a, head_dim, sparse, penalty, s);
+  }
+  return launch_attn_f32(a, head_dim, sparse, penalty, s);
+}
+
+// ------------------------------------------------------------- partition plan
+struct Run { int a, b; };
+struct Frame { int a, b; float t; };
+
+std::vector<Run> runs_where(const uint8_t* seg, int n, bool (*pred)(uint8_t)) {
+  std::vector<Run> out;
+  int i = 0;
+  while (i < n) {
+    if (pred(seg[i])) {
+      int j = i;
+      while (j < n && pred(seg[j])) ++j;
+      out.push_back({i, j});
+      i = j;
+    } else {
+      ++i;
+    }
+  }
+  return out;
+}
+
+bool is_output(uint8_t s) { return s == H3_SEG_OUTPUT; }
+bool not_output(uint8_t s) { return s != H3_SEG_OUTPUT; }
+bool is_guide(uint8_t s) { return s == H3_SEG_GUIDE; }
+bool not_guide(uint8_t s) { return s != H3_SEG_GUIDE; }
+
+// Frames: maximal runs of equal timestamp inside the runs of one segment kind.
+std::vector<Frame> frames_of(const uint8_t* seg, const float* t, int n, bool (*pred)(uint8_t)) {
+  std::vector<Frame> out;
+  for (const Run& r : runs_where(seg, n, pred)) {
+    int s = r.a;
+    for (int i = r.a + 1; i <= r.b; ++i) {
+      if (i == r.b || t[i] != t[s]) {
+        out.push_back({s, i, t[s]});
+        s = i;
+      }
+    }
+  }
+  return out;
+}
+
+struct ViaPlan {
+  std::vector<Run> nonout_q, out_q, nonguide_k, guide_k;
+  std::vector<Frame> guide_f, out_f;
+  std::vector<Run> vt_ranges;       // key ranges with their own transposed v copy
+  std::vector<size_t> vt_off;       // byte offsets in the workspace
+  size_t acc_off = 0, acc_lse_off = 0, part_off = 0, part_lse_off = 0, total = 0;
+  int max_out_rows = 0;
+};
+
+ViaPlan make_plan(const uint8_t* seg, const float* t, int n, int heads, int head_dim,
+                  int dtype) {
+  ViaPlan p;
+  p.nonout_q = runs_where(seg, n, not_output);
+  p.out_q = runs_where(seg, n, is_output);
+  p.nonguide_k = runs_where(seg, n, not_guide);
+  p.guide_k = runs_where(seg, n, is_guide);
+  p.guide_f = frames_of(seg, t, n, is_guide);
+  p.out_f = frames_of(seg, t, n, is_output);
+  p.vt_ranges.push_back({0, n});
+  for (const Run& r : p.nonguide_k) p.vt_ranges.push_back(r);
+  for (const Run& r : p.guide_k) p.vt_ranges.push_back(r);
+  for (const Frame& f : p.guide_f) p.vt_ranges.push_back({f.a, f.b});
+  size_t off = 0;
+  if (dtype == H3_DTYPE_BF16) {
+    for (const Run& r : p.vt_ranges) {
+      p.vt_off.push_back(off);
+      off += align256(vt_bytes(r.b - r.a, heads, head_dim));
+    }
+  }
+  for (const Run& r : p.out_q) p.max_out_rows = std::max(p.max_out_rows, r.b - r.a);
+  const size_t pairs = (size_t)p.max_out_rows * heads;
+  p.acc_off = off;
+  off += align256(pairs * head_dim * sizeof(float));
+  p.acc_lse_off = off;
+  off += align256(pairs * sizeof(float));
+  p.part_off = off;
+  off += align256(pairs * head_dim * sizeof(float));
+  p.part_lse_off = off;
+  off += align256(pairs * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+int vt_slot(const ViaPlan& p, int a, int b) {
+  for (size_t i = 0; i < p.vt_ranges.size(); ++i)
+    if (p.vt_ranges[i].a == a && p.vt_ranges[i].b == b) return (int)i;
+  return -1;
+}
+
+double host_penalty(double dt, double strength, double window, double falloff, double cap) {
+  const double x = std::max(dt - window, 0.0) / falloff;
+  return std::min(strength * x * x, cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_version(void) { return kVersion; }
+
+const char* h3attn_status_string(int status) {
+  switch (status) {
+    case H3_OK: return "ok";
+    case H3_EINVAL: return "invalid argument";
+    case H3_EUNSUPPORTED: return "unsupported dtype, head_dim or block_size";
+    case H3_ELAUNCH: return "kernel launch failed";
+    case H3_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t attn_dense_tara_workspace(int nk, int heads, int head_dim, int dtype) {
+  if (nk <= 0 || heads <= 0 || !dim_ok(head_dim) || dtype != H3_DTYPE_BF16) return 0;
+  return vt_bytes(nk, heads, head_dim);
+}
+
+int attn_dense_tara(const void* q, const void* k, const void* v, int dtype, int nq, int nk,
+                    int heads, int head_dim, const uint8_t* q_seg, const float* q_t,
+                    const uint8_t* k_seg, const float* k_t, float strength, float window,
+                    float falloff, float cap, float scale, void* o, int o_dtype, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !q_seg || !q_t || !k_seg || !k_t || !o || !lse) return H3_EINVAL;
+  if (nq <= 0 || nk <= 0 || heads <= 0) return H3_EINVAL;
+  if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || heads > 65535)
+    return H3_EUNSUPPORTED;
+  const size_t need = attn_dense_tara_workspace(nk, heads, head_dim, dtype);
+  if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
+  AttnArgs a = make_args(q, k, v, nq, nk, heads, q_seg, q_t, k_seg, k_t, strength, window,
+                         falloff, cap, scale, o, o_dtype, lse);
+  const bool pen = strength > 0.f && cap > 0.f;
+  hipError_t e = run_attention(a, dtype, head_dim, false, pen, (uint16_t*)ws, false,
+                               (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, int block_size,
+                     double sparsity_ratio, int* nb, int* n_video, int* n_prot, int* k_sel) {
+  if (!seg_host || n <= 0) return H3_EINVAL;
+  if (protected_prefix_len < 0 || protected_prefix_len > n) return H3_EINVAL;
+  if (!std::isfinite(sparsity_ratio) || sparsity_ratio < 0.0 || sparsity_ratio >= 1.0)
+    return H3_EINVAL;
+  if (block_size != kTile) return H3_EUNSUPPORTED;
+  const int blocks = (n + kTile - 1) / kTile;
+  int prot = 0;
+  for (int b = 0; b < blocks; ++b) {
+    const int lo = b * kTile, hi = std::min(n, lo + kTile);
+    bool p = lo < protected_prefix_len;
+    for (int r = lo; r < hi && !p; ++r)
+      p = seg_host[r] == H3_SEG_TEXT || seg_host[r] == H3_SEG_AUDIO;
+    prot += p ? 1 : 0;
+  }
+  const int video = blocks - prot;
+  int k = 0;
+  if (video > 0) {
+    if (sparsity_ratio == 0.0) {
+      k = video;
+    } else {
+      k = (int)std::ceil((1.0 - sparsity_ratio) * (double)video - 1e-9);
+      k = std::min(video, std::max(1, k));
+    }
+  }
+  if (nb) *nb = blocks;
+  if (n_video) *n_video = video;
+  if (n_prot) *n_prot = prot;
+  if (k_sel) *k_sel = k;
+  return H3_OK;
+}
+
+size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size) {
+  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || block_size != kTile) return 0;
+  return router_ws_bytes(n, heads, head_dim);
+}
+
+int attn_block_router(const void* q, const void* k, int dtype, int n, int heads, int head_dim,
+                      const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
+                      int32_t* tiles, int32_t* prot, int n_prot, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!q || !k || !seg || n <= 0 || heads <= 0) return H3_EINVAL;
+  if (protected_prefix_len < 0 || protected_prefix_len > n) return H3_EINVAL;
+  if (k_sel < 0 || n_prot < 0 || (k_sel > 0 && !tiles) || (n_prot > 0 && !prot))
+    return H3_EINVAL;
+  if (!dtype_ok(dtype) || !dim_ok(head_dim) || block_size != kTile || heads > 65535)
+    return H3_EUNSUPPORTED;
+  const int nb = (n + kTile - 1) / kTile;
+  if (k_sel > nb) return H3_EINVAL;
+  if (nb > router_max_blocks()) return H3_EUNSUPPORTED;
+  const size_t need = router_ws_bytes(n, heads, head_dim);
+  if (!ws || ws_bytes < need) return H3_EWORKSPACE;
+  RouterWs w = router_ws_carve(ws, n, heads, head_dim);
+  hipError_t e = launch_router(q, k, dtype == H3_DTYPE_BF16, n, heads, head_dim, seg,
+                               protected_prefix_len, k_sel, tiles, prot, n_prot, w,
+                               (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype) {
+  return attn_dense_tara_workspace(n, heads, head_dim, dtype);
+}
+
+int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, int n, int heads,
+                      int head_dim, const uint8_t* seg, const float* t, float strength,
+                      float window, float falloff, float cap, float scale, int block_size,
+                      const int32_t* tiles, int k_sel, const int32_t* prot, int n_prot, void* o,
+                      int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !seg || !t || !o || !lse) return H3_EINVAL;
+  if (n <= 0 || heads <= 0) return H3_EINVAL;
+  if (k_sel < 0 || n_prot < 0 || k_sel + n_prot == 0) return H3_EINVAL;
+  if ((k_sel > 0 && !tiles) || (n_prot > 0 && !prot)) return H3_EINVAL;
+  if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || block_size != kTile ||
+      heads > 65535)
+    return H3_EUNSUPPORTED;
+  const size_t need = attn_block_sparse_workspace(n, heads, head_dim, dtype);
+  if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
+  AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
+                         scale, o, o_dtype, lse);
+  a.prot = prot;
+  a.n_prot = n_prot;
+  a.tiles = tiles;
+  a.k_sel = k_sel;
+  a.nqb = (n + kTile - 1) / kTile;
+  const bool pen = strength > 0.f && cap > 0.f;
+  hipError_t e = run_attention(a, dtype, head_dim, true, pen, (uint16_t*)ws, false,
+                               (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,
+                        float log_w, const float* log_w_rows, int rows, int heads, int head_dim,
+                        void* stream) {
+  if (!o_acc || !lse_acc || !o_i || !lse_i || rows <= 0 || heads <= 0) return H3_EINVAL;
+  if (std::isnan(log_w) || log_w == INFINITY) return H3_EINVAL;
+  if (!dim_ok(head_dim)) return H3_EUNSUPPORTED;
+  if (log_w == -INFINITY) return H3_OK;
+  hipError_t e = launch_lse_merge(o_acc, lse_acc, o_i, lse_i, log_w, log_w_rows,
+                                  (int64_t)rows * heads, head_dim, (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+size_t attn_dense_tara_via_workspace(const uint8_t* seg_host, const float* t_host, int n,
+                                     int heads, int head_dim, int dtype) {
+  if (!seg_host || !t_host || n <= 0 || heads <= 0 || !dim_ok(head_dim) || !dtype_ok(dtype))
+    return 0;
+  return make_plan(seg_host, t_host, n, heads, head_dim, dtype).total;
+}
+
+int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, int n, int heads,
+                        int head_dim, const uint8_t* seg, const float* t,
+                        const uint8_t* seg_host, const float* t_host, float strength,
+                        float window, float falloff, float cap, float scale, void* o,
+                        int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !seg || !t || !seg_host || !t_host || !o || !lse) return H3_EINVAL;
+  if (n <= 0 || heads <= 0) return H3_EINVAL;
+  if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || heads > 65535)
+    return H3_EUNSUPPORTED;
+  const ViaPlan p = make_plan(seg_host, t_host, n, heads, head_dim, dtype);
+  if (!ws || ws_bytes < p.total) return H3_EWORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const int D = head_dim;
+  const size_t esz = dtype == H3_DTYPE_BF16 ? 2 : 4;
+  const size_t row_elems = (size_t)heads * D;
+  auto qrow = [&](int r) { return (const char*)q + (size_t)r * row_elems * esz; };
+  auto krow = [&](int r) { return (const char*)k + (size_t)r * row_elems * esz; };
+  auto vrow = [&](int r) { return (const char*)v + (size_t)r * row_elems * esz; };
+  float* acc = (float*)(w + p.acc_off);
+  float* acc_lse = (float*)(w + p.acc_lse_off);
+  float* part = (float*)(w + p.part_off);
+  float* part_lse = (float*)(w + p.part_lse_off);
+
+  // Transposed v copies, one per key range used below.
+  if (dtype == H3_DTYPE_BF16) {
+    for (size_t i = 0; i < p.vt_ranges.size(); ++i) {
+      const Run& r = p.vt_ranges[i];
+      if (launch_vt_transpose((const uint16_t*)vrow(r.a), (uint16_t*)(w + p.vt_off[i]),
+                              r.b - r.a, heads, D, s) != hipSuccess)
+        return H3_ELAUNCH;
+    }
+  }
+  // Ordinary attention of query rows [qa, qb) over key rows [ka, kb) into (out, out_lse).
+  auto call = [&](int qa, int qb, int ka, int kb, void* out, int out_dtype,
+                  float* out_lse) -> bool {
+    AttnArgs a = make_args(qrow(qa), krow(ka), vrow(ka), qb - qa, kb - ka, heads, seg + qa,
+                           t + qa, seg + ka, t + ka, 0.f, window, falloff, cap, scale, out,
+                           out_dtype, out_lse);
+    uint16_t* vt = nullptr;
+    if (dtype == H3_DTYPE_BF16) vt = (uint16_t*)(w + p.vt_off[vt_slot(p, ka, kb)]);
+    return run_attention(a, dtype, D, false, false, vt, true, s) == hipSuccess;
+  };
+
+  // Queries outside the output video: one ordinary call over every key.
+  for (const Run& r : p.nonout_q) {
+    float* l = lse + (size_t)r.a * heads;
+    void* out = (char*)o + (size_t)r.a * row_elems * (o_dtype == H3_DTYPE_BF16 ? 2 : 4);
+    if (!call(r.a, r.b, 0, n, out, o_dtype, l)) return H3_ELAUNCH;
+  }
+  const double base = -(double)cap;  // log of the uniform guide multiplier exp(-cap)
+  for (const Run& r : p.out_q) {
+    const int rows = r.b - r.a;
+    const int64_t pairs = (int64_t)rows * heads;
+    if (launch_fill(acc, acc_lse, pairs, D, s) != hipSuccess) return H3_ELAUNCH;
+    auto merge = [&](int row0, int nrows, double log_w) -> bool {
+      return launch_lse_merge(acc + (size_t)row0 * row_elems, acc_lse + (size_t)row0 * heads,
+                              part, part_lse, (float)log_w, nullptr,
+                              (int64_t)nrows * heads, D, s) == hipSuccess;
+    };
+    for (const Run& kr : p.nonguide_k) {
+      if (!call(r.a, r.b, kr.a, kr.b, part, H3_DTYPE_F32, part_lse)) return H3_ELAUNCH;
+      if (!merge(0, rows, 0.0)) return H3_ELAUNCH;
+    }
+    for (const Run& kr : p.guide_k) {
+      if (!call(r.a, r.b, kr.a, kr.b, part, H3_DTYPE_F32, part_lse)) return H3_ELAUNCH;
+      if (!merge(0, rows, base)) return H3_ELAUNCH;
+    }
+    for (const Frame& f : p.out_f) {
+      if (f.a < r.a || f.b > r.b) continue;
+      for (const Frame& g : p.guide_f) {
+        const double pen = host_penalty(std::fabs((double)f.t - (double)g.t), strength, window,
+                                        falloff, cap);
+        const double corr = std::expm1((double)cap - pen);  // exp(-p) - exp(-cap), / exp(-cap)
+        if (!(corr > 0.0)) continue;                        // zero-weight correction
+        if (!call(f.a, f.b, g.a, g.b, part, H3_DTYPE_F32, part_lse)) return H3_ELAUNCH;
+        if (!merge(f.a - r.a, f.b - f.a, base + std::log(corr))) return H3_ELAUNCH;
+      }
+    }
+    void* out = (char*)o + (size_t)r.a * row_elems * (o_dtype == H3_DTYPE_BF16 ? 2 : 4);
+    if (launch_finalize(acc, acc_lse, out, o_dtype == H3_DTYPE_F32,
+                        lse + (size_t)r.a * heads, pairs, D, s) != hipSuccess)
+      return H3_ELAUNCH;
+  }
+  return H3_OK;
+}
+
+}  // extern "C"

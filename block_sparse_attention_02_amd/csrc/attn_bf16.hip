@@ -1,0 +1,432 @@
+// bf16 attention for gfx950: dense TARA and block-sparse over 64-key tiles.
+//
+// Score rule ("Flash Partitions for H3 native temporal alignment", section 1):
+//   s_ij = scale * q_i.k_j - p_ij, p_ij = min(strength*(max(|t_i-t_j|-window,0)/falloff)^2, cap)
+//   only for (output-video query, guide-video key) pairs.
+// The penalty is computed in registers per 64-key tile. A tile whose 64 keys are all
+// guide rows of one frame gets a per-query scalar penalty (all spatial tokens of a
+// frame share the same temporal correction, section 3); mixed and ragged tiles take a
+// per-element path. No rows x rows bias is ever formed.
+//
+// Work decomposition (one workgroup = 4 waves of 64 lanes):
+//   dense : 128 query rows, wave w owns rows 32w..32w+31 and all 64 keys of each tile;
+//   sparse: one 64-row query block, wave w owns rows 32(w%2).. and keys 32(w/2).. of
+//           each routed tile; the two key halves are merged at the end.
+// Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
+// lane holds one query column; softmax row reductions stay in registers plus one
+// exchange between lane halves.
+// K and V^T tiles are double-buffered in LDS with an XOR swizzle on 16-byte chunks
+// (bank-conflict-free operand reads), prefetched through registers one tile ahead.
+// V^T comes from a transposed copy of v whose keys are permuted within 16-key groups
+// (bits 2 and 3 of the key index swapped) so that the probability registers produced by
+// the first product are directly the B operand of the second.
+#include "h3_internal.h"
+
+namespace h3 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima are only raised when a tile exceeds them by more than this (log2
+// units); probabilities then stay below 2^8 and most tiles skip the O rescale.
+constexpr float kLazyRescale = 8.0f;
+
+// Position of key `key` inside its 16-key group of the transposed v copy.
+__host__ __device__ constexpr int key_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+// Lanes l and l^32 hold the two key halves of the same query column.
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ __forceinline__ float tara_pen(float dt, float window, float inv_falloff,
+                                          float strength, float cap) {
+  float x = fmaxf(dt - window, 0.f) * inv_falloff;
+  return fminf(strength * (x * x), cap);
+}
+
+// ------------------------------------------------------------------ v transpose
+// vt[h][d][pos] = v[key][h][d] with pos = key_pos(key) inside each 16-key group;
+// keys past nk are zero so padded tiles contribute nothing.
+template <int D>
+__global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t* __restrict__ v,
+                                                           uint16_t* __restrict__ vt, int nk,
+                                                           int nkp, int H) {
+  constexpr int LD = D + 2;  // padded row so the column reads spread over banks
+  constexpr int CPR = D / 8;
+  __shared__ uint16_t tile[64 * LD];
+  const int k0 = blockIdx.x * 64;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, ch = c % CPR;
+    const int key = k0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < nk) val = *(const u32x4*)(v + ((int64_t)key * H + h) * D + ch * 8);
+    uint32_t* dst = (uint32_t*)(tile + r * LD + ch * 8);
+    dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
+  }
+  __syncthreads();
+  for (int c = tid; c < D * 8; c += 256) {
+    const int d = c / 8, pc = c % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = tile[key_pos(pc * 8 + 2 * j) * LD + d];
+      const uint32_t hi = tile[key_pos(pc * 8 + 2 * j + 1) * LD + d];
+      w[j] = lo | (hi << 16);
+    }
+    u32x4 out = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(vt + ((int64_t)h * D + d) * nkp + k0 + pc * 8) = out;
+  }
+}
+
+// ------------------------------------------------------------------ attention
+template <int D, int ROWG, int KSPLIT, bool SPARSE, bool PEN>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(ROWG * KSPLIT == 4, "four waves per workgroup");
+  constexpr int BM = 32 * ROWG;       // query rows per workgroup
+  constexpr int KW = 64 / KSPLIT;     // keys of a tile handled by one wave
+  constexpr int NT = KW / 32;         // 32x32 score tiles per wave
+  constexpr int NS = KW / 16;         // k-steps of the PV product
+  constexpr int DK = D / 16;          // k-steps of the QK product
+  constexpr int DT = D / 32;          // 32-row output tiles (over d)
+  constexpr int KCH = 64 * D / 8;     // 16-byte chunks per K tile
+  constexpr int VCH = D * 8;          // 16-byte chunks per V^T tile
+  constexpr int KPT = KCH / 256;
+  constexpr int VPT = VCH / 256;
+  constexpr int CPR = D / 8;          // 16-byte chunks per K row
+
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * 64];
+  __shared__ uint8_t kseg_s[2][64];
+  __shared__ float kt_s[2][64];
+  __shared__ int info_s[2];     // bit0 any guide key, bit1 all keys guide of one frame,
+                                // bit2 all 64 keys valid, bit3 tile skipped
+  __shared__ float tuni_s[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = wave % ROWG;
+  const int kh = wave / ROWG;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int qblk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int H = a.H;
+  const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
+  const uint16_t* __restrict__ kp = (const uint16_t*)a.k;
+  const uint16_t* __restrict__ vtp = a.vt;
+  const float c_log2 = a.scale * kLog2e;
+
+  const int qrow = qblk * BM + rg * 32 + l32;
+  const bool qvalid = qrow < a.nq;
+  bf16x8 qreg[DK];
+#pragma unroll
+  for (int s = 0; s < DK; ++s) {
+    if (qvalid) {
+      qreg[s] = *(const bf16x8*)(qp + ((int64_t)qrow * H + h) * D + 16 * s + 8 * hh);
+    } else {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qreg[s] = __builtin_bit_cast(bf16x8, z);
+    }
+  }
+  const float qt = qvalid ? a.q_t[qrow] : 0.f;
+  const bool q_out = PEN && qvalid && a.q_seg[qrow] == kSegOutput;
+  const bool wave_out = PEN && (__ballot(q_out) != 0ull);
+
+  const int nkb = (a.nk + 63) / 64;
+  int ntiles;
+  const int32_t* rt = nullptr;
+  if (SPARSE) {
+    ntiles = a.n_prot + a.k_sel;
+    rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
+  } else {
+    ntiles = nkb;
+  }
+  auto tile_of = [&](int i) -> int {
+    if (!SPARSE) return i;
+    return i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
+  };
+
+  u32x4 kreg[KPT];
+  u32x4 vreg[VPT];
+  uint32_t sreg = kSegInvalid;
+  float treg = 0.f;
+
+  auto gload = [&](int kb) {
+    if (kb >= 0 && kb < nkb) {
+      const int k0 = kb * 64;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int c = tid + i * 256;
+        const int r = c / CPR, ch = c % CPR;
+        const int key = min(k0 + r, a.nk - 1);  // ragged tail: clamped, masked later
+        kreg[i] = *(const u32x4*)(kp + ((int64_t)key * H + h) * D + ch * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = tid + i * 256;
+        const int d = c >> 3, ch = c & 7;
+        vreg[i] = *(const u32x4*)(vtp + ((int64_t)h * D + d) * a.nkp + k0 + ch * 8);
+      }
+      if (tid < 64) {
+        const int key = k0 + tid;
+        const bool kv = key < a.nk;
+        sreg = kv ? (uint32_t)a.k_seg[key] : (uint32_t)kSegInvalid;
+        treg = kv ? a.k_t[key] : 0.f;
+      }
+    } else {
+      if (tid < 64) { sreg = kSegInvalid; treg = 0.f; }
+    }
+  };
+
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / CPR, ch = c % CPR;
+      *(u32x4*)&ks[st][r * D + ((ch ^ (r & 7)) * 8)] = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * 256;
+      const int d = c >> 3, ch = c & 7;
+      *(u32x4*)&vs[st][d * 64 + ((ch ^ (d & 7)) * 8)] = vreg[i];
+    }
+    if (tid < 64) {
+      kseg_s[st][tid] = (uint8_t)sreg;
+      kt_s[st][tid] = treg;
+      const uint64_t g = __ballot(sreg == (uint32_t)kSegGuide);
+      const uint64_t valid = __ballot(sreg != (uint32_t)kSegInvalid);
+      const float t0 = __shfl(treg, 0);
+      const uint64_t same = __ballot(treg == t0);
+      if (tid == 0) {
+        int info = 0;
+        if (g) info |= 1;
+        if (g == ~0ull && same == ~0ull) info |= 2;
+        if (valid == ~0ull) info |= 4;
+        if (valid == 0ull) info |= 8;
+        info_s[st] = info;
+        tuni_s[st] = t0;
+      }
+    }
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  if (ntiles > 0) {
+    gload(tile_of(0));
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) gload(tile_of(it + 1));
+    const int info = __builtin_amdgcn_readfirstlane(info_s[st]);
+    if (!(info & 8)) {
+      // ---- S^T = K Q^T (keys as rows, this wave's 32 queries as columns)
+      f32x16 sacc[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
+      const uint16_t* kst = ks[st];
+#pragma unroll
+      for (int s = 0; s < DK; ++s) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int kr = kh * KW + 32 * c + l32;
+          const bf16x8 ka = *(const bf16x8*)&kst[kr * D + (((2 * s + hh) ^ (kr & 7)) * 8)];
+          sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
+        }
+      }
+
+      // ---- scores in log2 units: x = s*scale*log2e - pen*log2e
+      float cc = c_log2, bb = 0.f, tmax;
+      const bool full = (info & 4) != 0;
+      const bool pen_tile = PEN && wave_out && (info & 1);
+      if (full && (!pen_tile || (info & 2))) {
+        if (pen_tile) {
+          const float p = tara_pen(fabsf(qt - tuni_s[st]), a.window, a.inv_falloff, a.strength,
+                                   a.cap);
+          bb = q_out ? -p * kLog2e : 0.f;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
+        tmax = mx * cc + bb;
+      } else {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kl = kh * KW + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const uint32_t sg = kseg_s[st][kl];
+            float x = sacc[c][r] * cc;
+            if (sg == (uint32_t)kSegInvalid) {
+              x = -INFINITY;
+            } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
+              x -= tara_pen(fabsf(qt - kt_s[st][kl]), a.window, a.inv_falloff, a.strength,
+                            a.cap) * kLog2e;
+            }
+            sacc[c][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        cc = 1.f;
+        tmax = mx;
+      }
+      tmax = pair_max(tmax);
+
+      // ---- online softmax with lazy rescale
+      if (__ballot(tmax > m_run + kLazyRescale) != 0ull) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mb = bb - (m_run == -INFINITY ? 0.f : m_run);
+      bf16x8 pb[NS];
+      float rs = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
+          rs += p;
+          pv[e] = p;
+        }
+        pb[s] = __builtin_convertvector(pv, bf16x8);
+      }
+      l_run += rs;
+
+      // ---- O^T += V^T P^T
+      const uint16_t* vst = vs[st];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dr = 32 * dt + l32;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int ch = kh * (KW / 8) + 2 * s + hh;
+          const bf16x8 va = *(const bf16x8*)&vst[dr * 64 + ((ch ^ (dr & 7)) * 8)];
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- combine lane halves, then key halves (sparse), then normalise
+  float l_tot = pair_sum(l_run);
+  if (KSPLIT == 2) {
+    float* ox = (float*)&ks[0][0];  // [ROWG][DT*16][64]
+    float* ml = (float*)&vs[0][0];  // [ROWG][2][64]
+    if (kh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ox[(rg * DT * 16 + dt * 16 + r) * 64 + lane] = oacc[dt][r];
+      ml[(rg * 2 + 0) * 64 + lane] = m_run;
+      ml[(rg * 2 + 1) * 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = ml[(rg * 2 + 0) * 64 + lane];
+      const float l1 = ml[(rg * 2 + 1) * 64 + lane];
+      const float M = fmaxf(m_run, m1);
+      const float a0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float a1 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[dt][r] = oacc[dt][r] * a0 + ox[(rg * DT * 16 + dt * 16 + r) * 64 + lane] * a1;
+      l_tot = l_tot * a0 + l1 * a1;
+      m_run = M;
+    }
+  }
+  if (kh == 0 && qvalid) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t obase = ((int64_t)qrow * H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 ov;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[j] = oacc[dt][4 * g + j] * inv;
+        const int d = 32 * dt + 8 * g + 4 * hh;
+        if (a.o_f32) {
+          *(f32x4*)((float*)a.o + obase + d) = ov;
+        } else {
+          *(bf16x4*)((__bf16*)a.o + obase + d) = __builtin_convertvector(ov, bf16x4);
+        }
+      }
+    }
+    if (hh == 0)
+      a.lse[(int64_t)qrow * H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool SPARSE, bool PEN>
+hipError_t launch_variant(const AttnArgs& a, hipStream_t s) {
+  if (SPARSE) {
+    dim3 grid(a.nqb, a.H);
+    attn_bf16_kernel<D, 2, 2, true, PEN><<<grid, 256, 0, s>>>(a);
+  } else {
+    dim3 grid((a.nq + 127) / 128, a.H);
+    attn_bf16_kernel<D, 4, 1, false, PEN><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vt_transpose(const uint16_t* v, uint16_t* vt, int nk, int H, int D,
+                               hipStream_t s) {
+  const int nkp = (int)pad_keys(nk);
+  dim3 grid(nkp / 64, H);
+  if (D == 128)
+    vt_transpose_kernel<128><<<grid, 256, 0, s>>>(v, vt, nk, nkp, H);
+  else
+    vt_transpose_kernel<64><<<grid, 256, 0, s>>>(v, vt, nk, nkp, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s) {
+  if (D == 128) {
+    if (sparse) return penalty ? launch_variant<128, true, true>(a, s) : launch_variant<128, true, false>(a, s);
+    return penalty ? launch_variant<128, false, true>(a, s) : launch_variant<128, false, false>(a, s);
+  }
+  if (sparse) return penalty ? launch_variant<64, true, true>(a, s) : launch_variant<64, true, false>(a, s);
+  return penalty ? launch_variant<64, false, true>(a, s) : launch_variant<64, false, false>(a, s);
+}
+
+}  // namespace h3

@@ -1,0 +1,146 @@
+// float32 attention (dense TARA and block-sparse) on the vector ALUs.
+//
+// Same score rule as the bf16 path ("Flash Partitions for H3 native temporal
+// alignment", section 1) with every product, exponential and sum in float32, so
+// float32 inputs are never rounded to bf16. One lane owns one query row; keys are
+// staged 16 at a time in LDS and read as broadcasts. This path serves float32
+// callers and small problems; the matrix-core path serves bf16.
+#include "h3_internal.h"
+
+namespace h3 {
+namespace {
+
+constexpr int kSub = 16;
+
+template <int D, bool SPARSE, bool PEN>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  __shared__ float ksh[kSub][D];
+  __shared__ float vsh[kSub][D];
+  __shared__ uint32_t sgs[kSub];
+  __shared__ float tss[kSub];
+
+  const int lane = threadIdx.x;
+  const int qblk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int H = a.H;
+  const float* __restrict__ qp = (const float*)a.q;
+  const float* __restrict__ kp = (const float*)a.k;
+  const float* __restrict__ vp = (const float*)a.v;
+  const int qrow = qblk * 64 + lane;
+  const bool qvalid = qrow < a.nq;
+
+  float q[D];
+  float o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = qvalid ? qp[((int64_t)qrow * H + h) * D + d] : 0.f;
+    o[d] = 0.f;
+  }
+  const float qt = qvalid ? a.q_t[qrow] : 0.f;
+  const bool q_out = PEN && qvalid && a.q_seg[qrow] == kSegOutput;
+  float m = -INFINITY, l = 0.f;
+
+  const int nkb = (a.nk + 63) / 64;
+  int ntiles;
+  const int32_t* rt = nullptr;
+  if (SPARSE) {
+    ntiles = a.n_prot + a.k_sel;
+    rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
+  } else {
+    ntiles = nkb;
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    int kb = it;
+    if (SPARSE) kb = it < a.n_prot ? a.prot[it] : rt[it - a.n_prot];
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    if (kb < 0 || kb >= nkb) continue;
+    for (int sub = 0; sub < 64 / kSub; ++sub) {
+      const int k0 = kb * 64 + sub * kSub;
+      if (k0 >= a.nk) break;
+      __syncthreads();
+      for (int e = lane; e < kSub * D; e += 64) {
+        const int j = e / D, d = e % D;
+        const int key = k0 + j;
+        const bool kv = key < a.nk;
+        ksh[j][d] = kv ? kp[((int64_t)key * H + h) * D + d] : 0.f;
+        vsh[j][d] = kv ? vp[((int64_t)key * H + h) * D + d] : 0.f;
+      }
+      if (lane < kSub) {
+        const int key = k0 + lane;
+        const bool kv = key < a.nk;
+        sgs[lane] = kv ? (uint32_t)a.k_seg[key] : (uint32_t)kSegInvalid;
+        tss[lane] = kv ? a.k_t[key] : 0.f;
+      }
+      __syncthreads();
+      float sc[kSub];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kSub; ++j) {
+        float dot = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) dot = fmaf(q[d], ksh[j][d], dot);
+        float x = dot * a.scale;
+        const uint32_t sg = sgs[j];
+        if (sg == (uint32_t)kSegInvalid) {
+          x = -INFINITY;
+        } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
+          const float dt = fabsf(qt - tss[j]);
+          const float u = fmaxf(dt - a.window, 0.f) * a.inv_falloff;
+          x -= fminf(a.strength * (u * u), a.cap);
+        }
+        sc[j] = x;
+        smax = fmaxf(smax, x);
+      }
+      if (smax > m) {
+        const float alpha = expf(m - smax);  // m = -inf gives 0
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] *= alpha;
+        l *= alpha;
+        m = smax;
+      }
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+          const float p = expf(sc[j] - m);
+          l += p;
+#pragma unroll
+          for (int d = 0; d < D; ++d) o[d] = fmaf(p, vsh[j][d], o[d]);
+        }
+      }
+    }
+  }
+  if (!qvalid) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t ob = ((int64_t)qrow * H + h) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const float val = o[d] * inv;
+    if (a.o_f32)
+      ((float*)a.o)[ob + d] = val;
+    else
+      ((__bf16*)a.o)[ob + d] = (__bf16)val;
+  }
+  a.lse[(int64_t)qrow * H + h] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+template <int D, bool SPARSE, bool PEN>
+hipError_t launch_f32_variant(const AttnArgs& a, hipStream_t s) {
+  const int nblk = SPARSE ? a.nqb : (a.nq + 63) / 64;
+  dim3 grid(nblk, a.H);
+  attn_f32_kernel<D, SPARSE, PEN><<<grid, 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s) {
+  if (D == 128) {
+    if (sparse) return penalty ? launch_f32_variant<128, true, true>(a, s) : launch_f32_variant<128, true, false>(a, s);
+    return penalty ? launch_f32_variant<128, false, true>(a, s) : launch_f32_variant<128, false, false>(a, s);
+  }
+  if (sparse) return penalty ? launch_f32_variant<64, true, true>(a, s) : launch_f32_variant<64, true, false>(a, s);
+  return penalty ? launch_f32_variant<64, false, true>(a, s) : launch_f32_variant<64, false, false>(a, s);
+}
+
+}  // namespace h3

@@ -1,0 +1,70 @@
+// Internal declarations shared by the HIP translation units of libh3attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h3 {
+
+constexpr int kTile = 64;         // key tile = routing block = 64 rows
+constexpr int kSegText = 0, kSegGuide = 1, kSegAudio = 2, kSegOutput = 3;
+constexpr int kSegInvalid = 255;  // marks key slots past the end of a tile
+
+// Arguments of one attention launch (dense or block-sparse).
+struct AttnArgs {
+  const void* q;            // [nq][H][D]  (bf16 bits or f32)
+  const void* k;            // [nk][H][D]
+  const void* v;            // [nk][H][D]  (f32 path)
+  const uint16_t* vt;       // [H][D][nkp] bf16, keys permuted in 16-groups (bf16 path)
+  const uint8_t* q_seg;
+  const float* q_t;
+  const uint8_t* k_seg;
+  const float* k_t;
+  void* o;                  // [nq][H][D]
+  float* lse;               // [nq][H]
+  int nq, nk, nkp, H;
+  int o_f32;                // 1: o is float32, 0: bf16
+  float scale;
+  float strength, window, inv_falloff, cap;
+  // block-sparse tile lists (unused by the dense launch)
+  const int32_t* prot;
+  int n_prot;
+  const int32_t* tiles;     // [H][nqb][k_sel]
+  int k_sel;
+  int nqb;
+};
+
+// Rounds a key count up to whole 64-key tiles.
+inline int64_t pad_keys(int64_t nk) { return (nk + kTile - 1) / kTile * kTile; }
+
+// bf16 path: transposes v into vt (see attn_bf16.hip), then runs attention.
+hipError_t launch_vt_transpose(const uint16_t* v, uint16_t* vt, int nk, int H, int D,
+                               hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
+// float32 path.
+hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
+
+// Router.
+struct RouterWs {
+  float* qbar;     // [H][nb][D]
+  float* kbar;     // [H][nb][D]
+  int32_t* video;  // [nb]
+  int32_t* counts; // [2]: n_prot, n_video
+};
+size_t router_ws_bytes(int n, int H, int D);
+RouterWs router_ws_carve(void* ws, int n, int H, int D);
+int router_max_blocks();
+hipError_t launch_router(const void* q, const void* k, bool bf16, int n, int H, int D,
+                         const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
+                         int32_t* prot, int prot_cap, const RouterWs& w, hipStream_t s);
+
+// LSE merge and accumulator finalisation.
+hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,
+                            float log_w, const float* log_w_rows, int64_t pairs, int D,
+                            hipStream_t s);
+hipError_t launch_fill(float* o_acc, float* lse_acc, int64_t pairs, int D, hipStream_t s);
+hipError_t launch_finalize(const float* o_acc, const float* lse_acc, void* o, int o_f32,
+                           float* lse, int64_t pairs, int D, hipStream_t s);
+
+}  // namespace h3

@@ -1,0 +1,324 @@
+// Pooled block router for block-sparse attention.
+//
+// "H3 SLA Attention", "How it works": every query block is scored against every key
+// block by one small pooled Q/K product, and only the best (1 - sparsity) share is
+// attended; inputs table: blocks overlapping language or audio rows are always attended.
+// "H3 sparse-attention breakpoints": the density is a fraction of the video KV tiles.
+//
+// Three kernels, all deterministic (no floating-point atomics):
+//   1. flags   : protected / video classification of the 64-row blocks and their
+//                ascending lists (one workgroup, ballot-based compaction);
+//   2. pool    : per-block means of q and k, float32 sums in row order, one pass over
+//                q and k in HBM (memory bound);
+//   3. score+top-k: per head and group of query blocks, pooled scores against every
+//                video tile in LDS (float32 products added in order of d, no fused
+//                multiply-add), then an exact radix select of the k best per query block
+//                with ties to the lower tile index, emitted in ascending tile order.
+#include "h3_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace h3 {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTopkWaves = 4;
+
+// ------------------------------------------------------------------ 1. flags
+__global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __restrict__ seg,
+                                                            int n, int prefix, int nb,
+                                                            int32_t* __restrict__ prot,
+                                                            int prot_cap,
+                                                            int32_t* __restrict__ video,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int wsum_p[16], wsum_v[16];
+  __shared__ int base_p, base_v;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  if (tid == 0) { base_p = 0; base_v = 0; }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int start = 0; start < nb; start += 1024) {
+    const int b = start + tid;
+    const bool valid = b < nb;
+    bool isp = false;
+    if (valid) {
+      const int lo = b * kTile;
+      const int hi = min(n, lo + kTile);
+      isp = lo < prefix;
+      for (int r = lo; r < hi && !isp; ++r) {
+        const int s = seg[r];
+        isp = (s == kSegText) || (s == kSegAudio);
+      }
+    }
+    const bool isv = valid && !isp;
+    isp = valid && isp;
+    const uint64_t mp = __ballot(isp);
+    const uint64_t mv = __ballot(isv);
+    if (lane == 0) { wsum_p[w] = __popcll(mp); wsum_v[w] = __popcll(mv); }
+    __syncthreads();
+    int offp = base_p, offv = base_v;
+    for (int j = 0; j < w; ++j) { offp += wsum_p[j]; offv += wsum_v[j]; }
+    const int ip = offp + __popcll(mp & below);
+    const int iv = offv + __popcll(mv & below);
+    if (isp && ip < prot_cap) prot[ip] = b;
+    if (isv) video[iv] = b;
+    __syncthreads();
+    if (tid == 0) {
+      int tp = 0, tv = 0;
+      for (int j = 0; j < 16; ++j) { tp += wsum_p[j]; tv += wsum_v[j]; }
+      base_p += tp;
+      base_v += tv;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) { counts[0] = base_p; counts[1] = base_v; }
+}
+
+// ------------------------------------------------------------------ 2. pool
+// Thread = 8 consecutive (head, d) elements of a row; workgroup = one 64-row block.
+template <bool BF16, int D>
+__global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict__ q,
+                                                          const void* __restrict__ k, int n,
+                                                          int H, int nb,
+                                                          float* __restrict__ qbar,
+                                                          float* __restrict__ kbar) {
+  const int b = blockIdx.x;
+  const int e0 = (blockIdx.y * 128 + threadIdx.x) * 8;
+  if (e0 >= H * D) return;
+  const int h = e0 / D, d0 = e0 % D;
+  const int lo = b * kTile, hi = min(n, lo + kTile);
+  const int64_t rs = (int64_t)H * D;
+  float aq[8], ak[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { aq[i] = 0.f; ak[i] = 0.f; }
+#pragma unroll 8
+  for (int r = lo; r < hi; ++r) {
+    const int64_t off = (int64_t)r * rs + e0;
+    float xq[8], xk[8];
+    if (BF16) {
+      const u32x4 uq = *(const u32x4*)((const uint16_t*)q + off);
+      const u32x4 uk = *(const u32x4*)((const uint16_t*)k + off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xq[2 * i] = __uint_as_float(uq[i] << 16);
+        xq[2 * i + 1] = __uint_as_float(uq[i] & 0xFFFF0000u);
+        xk[2 * i] = __uint_as_float(uk[i] << 16);
+        xk[2 * i + 1] = __uint_as_float(uk[i] & 0xFFFF0000u);
+      }
+    } else {
+      const f32x4* pq = (const f32x4*)((const float*)q + off);
+      const f32x4* pk = (const f32x4*)((const float*)k + off);
+      const f32x4 q0 = pq[0], q1 = pq[1], k0 = pk[0], k1 = pk[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xq[i] = q0[i]; xq[4 + i] = q1[i];
+        xk[i] = k0[i]; xk[4 + i] = k1[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      aq[i] = __fadd_rn(aq[i], xq[i]);
+      ak[i] = __fadd_rn(ak[i], xk[i]);
+    }
+  }
+  const float cnt = (float)(hi - lo);
+  float* oq = qbar + ((int64_t)h * nb + b) * D + d0;
+  float* ok = kbar + ((int64_t)h * nb + b) * D + d0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    oq[i] = __fdiv_rn(aq[i], cnt);
+    ok[i] = __fdiv_rn(ak[i], cnt);
+  }
+}
+
+// ------------------------------------------------------------------ 3. score + top-k
+// Order-preserving map of a float32 score to an unsigned key: larger key = better;
+// -0 and +0 map together; NaN maps below every number.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  if (s != s) return 0u;
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ qbar,
+                                                          const float* __restrict__ kbar,
+                                                          const int32_t* __restrict__ video,
+                                                          const int32_t* __restrict__ counts,
+                                                          int nb, int k_sel,
+                                                          int32_t* __restrict__ tiles) {
+  extern __shared__ float sc[];  // [QB][nv]
+  __shared__ float qs[QB][D];
+  __shared__ int hist[kTopkWaves][256];
+  const int h = blockIdx.y;
+  const int qb0 = blockIdx.x * QB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int nv = counts[1];
+
+  for (int e = tid; e < QB * D; e += 256) {
+    const int j = e / D, d = e % D;
+    qs[j][d] = (qb0 + j < nb) ? qbar[((int64_t)h * nb + qb0 + j) * D + d] : 0.f;
+  }
+  __syncthreads();
+  for (int vi = tid; vi < nv; vi += 256) {
+    const float* kr = kbar + ((int64_t)h * nb + video[vi]) * D;
+    float acc[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) acc[j] = 0.f;
+    for (int d0 = 0; d0 < D; d0 += 4) {
+      const f32x4 kv = *(const f32x4*)(kr + d0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < QB; ++j) acc[j] = __fadd_rn(acc[j], __fmul_rn(qs[j][d0 + i], kv[i]));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) sc[j * nv + vi] = acc[j];
+  }
+  __syncthreads();
+
+  // ---- exact selection: radix select of the k-th best key, 8 bits per pass
+  const bool active = w < QB;
+  const float* my = sc + (active ? w : 0) * nv;
+  const int kk = min(k_sel, nv);
+  const bool take_all = (kk == nv);
+  uint32_t prefix = 0u, pmask = 0u;
+  int rem = kk;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int j = lane; j < 256; j += 64) hist[w][j] = 0;
+    __syncthreads();
+    if (active && !take_all && kk > 0) {
+      for (int i = lane; i < nv; i += 64) {
+        const uint32_t key = order_key(my[i]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1);
+      }
+    }
+    __syncthreads();
+    if (active && !take_all && kk > 0) {
+      int c[4];
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[w][255 - 4 * lane - j]; sum += c[j]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const int excl = incl - sum;
+      const bool here = excl < rem && rem <= incl;
+      int digit = 0, above = 0;
+      if (here) {
+        int cum = excl;
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= rem) { digit = 255 - 4 * lane - j; above = cum; break; }
+          cum += c[j];
+        }
+      }
+      const uint64_t bm = __ballot(here);
+      const int src = __ffsll((unsigned long long)bm) - 1;
+      digit = __shfl(digit, src);
+      above = __shfl(above, src);
+      rem -= above;
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 0xFFu << shift;
+    }
+    __syncthreads();
+  }
+
+  const int qb = qb0 + w;
+  if (!active || qb >= nb || k_sel == 0) return;
+  int32_t* out = tiles + ((int64_t)h * nb + qb) * k_sel;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int pos = 0, eq_seen = 0;
+  for (int base = 0; base < nv; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < nv;
+    const uint32_t key = valid ? order_key(my[i]) : 0u;
+    bool gt, eq;
+    if (take_all) {
+      gt = valid;
+      eq = false;
+    } else {
+      gt = valid && kk > 0 && key > prefix;
+      eq = valid && kk > 0 && key == prefix;
+    }
+    const uint64_t eqm = __ballot(eq);
+    const int eq_rank = eq_seen + __popcll(eqm & below);
+    const bool sel = gt || (eq && eq_rank < rem);
+    const uint64_t selm = __ballot(sel);
+    if (sel) out[pos + __popcll(selm & below)] = video[i];
+    pos += __popcll(selm);
+    eq_seen += __popcll(eqm);
+  }
+  for (int j = kk + lane; j < k_sel; j += 64) out[j] = -1;
+}
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t router_ws_bytes(int n, int H, int D) {
+  const size_t nb = (size_t)((n + kTile - 1) / kTile);
+  return 2 * align256(nb * H * D * sizeof(float)) + align256(nb * sizeof(int32_t)) + 256;
+}
+
+RouterWs router_ws_carve(void* ws, int n, int H, int D) {
+  const size_t nb = (size_t)((n + kTile - 1) / kTile);
+  char* p = (char*)ws;
+  RouterWs w;
+  w.qbar = (float*)p;
+  p += align256(nb * H * D * sizeof(float));
+  w.kbar = (float*)p;
+  p += align256(nb * H * D * sizeof(float));
+  w.video = (int32_t*)p;
+  p += align256(nb * sizeof(int32_t));
+  w.counts = (int32_t*)p;
+  return w;
+}
+
+// Largest block count the score/top-k kernel keeps in LDS (QB x nb floats).
+int router_max_blocks() { return 14000; }
+
+hipError_t launch_router(const void* q, const void* k, bool bf16, int n, int H, int D,
+                         const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
+                         int32_t* prot, int prot_cap, const RouterWs& w, hipStream_t s) {
+  const int nb = (n + kTile - 1) / kTile;
+  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, prot, prot_cap, w.video, w.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int chunks = (H * D / 8 + 127) / 128;
+  dim3 pgrid(nb, chunks);
+  if (bf16) {
+    if (D == 128) router_pool_kernel<true, 128><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
+    else router_pool_kernel<true, 64><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
+  } else {
+    if (D == 128) router_pool_kernel<false, 128><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
+    else router_pool_kernel<false, 64><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool wide = (size_t)4 * nb * sizeof(float) <= 56 * 1024;
+  const int qb = wide ? 4 : 1;
+  dim3 tgrid((nb + qb - 1) / qb, H);
+  const size_t lds = (size_t)qb * nb * sizeof(float);
+  if (wide) {
+    if (D == 128) router_topk_kernel<128, 4><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+    else router_topk_kernel<64, 4><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+  } else {
+    if (D == 128) router_topk_kernel<128, 1><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+    else router_topk_kernel<64, 1><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h3

@@ -19,6 +19,8 @@ bf16 workloads, to bf16 (round to nearest even). Both sides read the same bits.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Iterable, Sequence
 
@@ -175,44 +177,68 @@ def _streams(w: Workload):
     return np.random.SeedSequence(1000 + w.seed_index).spawn(4 * w.heads)
 
 
-def _head_values(w: Workload, children, tensor: int, h: int, fid: np.ndarray,
-                 n_frames: int) -> np.ndarray:
+def _video_frames(w: Workload):
+    """(first row, last row + 1, global frame index) of every video frame."""
+    out = []
+    r = 0
+    nf = 0
+    for s in w.spans:
+        if s.frames:
+            per = s.length // s.frames
+            for f in range(s.frames):
+                out.append((r + f * per, r + (f + 1) * per, nf))
+                nf += 1
+        r += s.length
+    return out
+
+
+def _head_values(w: Workload, children, tensor: int, h: int, frames) -> np.ndarray:
     """float64 [n, d] values of one tensor for one head, before rounding."""
     rng = np.random.Generator(np.random.PCG64(children[tensor * w.heads + h]))
     z = rng.standard_normal((w.n, w.head_dim))
     if tensor == TENSOR_V:
         return z
-    if w.frame_weight > 0.0:
+    if w.frame_weight > 0.0 and frames:
         frng = np.random.Generator(np.random.PCG64(children[TENSOR_FRAME * w.heads + h]))
-        c = frng.standard_normal((n_frames, w.head_dim))
+        c = frng.standard_normal((len(frames), w.head_dim))
         a = w.frame_weight
         b = float(np.sqrt(1.0 - a * a))
-        vid = fid >= 0
-        z[vid] = a * c[fid[vid]] + b * z[vid]
+        for r0, r1, f in frames:
+            z[r0:r1] = a * c[f] + b * z[r0:r1]
     if w.qk_gain != 1.0:
         z = w.qk_gain * z
     return z
 
 
-def make_qkv(w: Workload, heads: Sequence[int] | None = None):
+def make_qkv(w: Workload, heads: Sequence[int] | None = None, workers: int | None = None):
     """Seeded q, k, v of shape [n, len(heads), d].
 
     fp32 workloads return float32 arrays; bf16 workloads return uint16 bf16
     bit patterns. ``heads`` selects a subset (the values of head ``h`` do not
-    depend on which other heads are drawn).
+    depend on which other heads are drawn). Streams are drawn in parallel
+    threads; every stream is independent, so the values do not depend on the
+    thread count.
     """
     hs = list(range(w.heads)) if heads is None else list(heads)
     children = _streams(w)
-    fid = frame_ids(w)
-    n_frames = int(fid.max()) + 1 if (fid >= 0).any() else 0
+    frames = _video_frames(w)
     out_dtype = np.float32 if w.dtype == "f32" else np.uint16
-    out = []
-    for tensor in (TENSOR_Q, TENSOR_K, TENSOR_V):
-        arr = np.empty((w.n, len(hs), w.head_dim), dtype=out_dtype)
-        for j, h in enumerate(hs):
-            x32 = _head_values(w, children, tensor, h, fid, n_frames).astype(np.float32)
-            arr[:, j, :] = x32 if w.dtype == "f32" else f32_to_bf16_bits(x32)
-        out.append(arr)
+    out = [np.empty((w.n, len(hs), w.head_dim), dtype=out_dtype) for _ in range(3)]
+
+    def fill(job):
+        tensor, j = job
+        x32 = _head_values(w, children, tensor, hs[j], frames).astype(np.float32)
+        out[tensor][:, j, :] = x32 if w.dtype == "f32" else f32_to_bf16_bits(x32)
+
+    jobs = [(tensor, j) for tensor in (TENSOR_Q, TENSOR_K, TENSOR_V) for j in range(len(hs))]
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1)
+    if workers <= 1 or len(jobs) == 1:
+        for job in jobs:
+            fill(job)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, jobs))
     return tuple(out)
 
 

@@ -1,0 +1,209 @@
+/*
+ * h3attn — TARA dense and pooled block-sparse attention for one packed
+ * sequence, hand-written HIP for gfx950 (MI355X).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Rows:      one packed sequence [text | guide video | audio | output video]
+ *            ("Flash Partitions for H3 native temporal alignment", section 1).
+ * q, k, v, o [rows][heads][head_dim], contiguous, row stride heads*head_dim.
+ * lse        [rows][heads] float32, natural log of the softmax normaliser.
+ *            A row sub-range of q/o/lse is a plain pointer offset.
+ * seg        [rows] uint8: 0 text (incl. padding), 1 guide video, 2 audio,
+ *            3 output video.
+ * t          [rows] float32 seconds (video frame k at k/6 s; 0 elsewhere).
+ * dtype      H3_DTYPE_F32 (0) or H3_DTYPE_BF16 (1, raw bf16 bit patterns).
+ * Pointers   named *_host are host memory; every other data pointer is device
+ *            memory on the current HIP device.
+ * stream     a hipStream_t (NULL = the null stream). Calls are stream-ordered
+ *            and asynchronous: they never synchronise with the host, and
+ *            results are valid once the stream has completed.
+ * Ownership  the caller allocates every buffer, including workspaces sized by
+ *            the *_workspace functions. The library allocates no device
+ *            memory and keeps no global state; calls are re-entrant. Calls
+ *            that share a workspace must be ordered on one stream.
+ * Errors     every argument check runs before any HIP call, so a bad call
+ *            returns without touching the device. Nothing throws across the
+ *            boundary.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3_OK            0
+#define H3_EINVAL       (-1)  /* null pointer, bad size, non-finite or out-of-range knob */
+#define H3_EUNSUPPORTED (-2)  /* dtype, head_dim not in {64,128}, block_size != 64 */
+#define H3_ELAUNCH      (-3)  /* a kernel launch failed (hipGetLastError) */
+#define H3_EWORKSPACE   (-4)  /* workspace pointer null or smaller than required */
+
+#define H3_DTYPE_F32  0
+#define H3_DTYPE_BF16 1
+
+#define H3_SEG_TEXT   0
+#define H3_SEG_GUIDE  1
+#define H3_SEG_AUDIO  2
+#define H3_SEG_OUTPUT 3
+
+/* Library version (major*10000 + minor*100 + patch). */
+int h3attn_version(void);
+
+/* Static text naming a status code. */
+const char* h3attn_status_string(int status);
+
+/*
+ * Dense TARA attention.
+ * Defined by "Flash Partitions for H3 native temporal alignment", section 1
+ * (restated in "TARA : alignement temporel natif pour les références MiniMax
+ * H3", "La règle temporelle"): for query row i and key row j of head h,
+ *   s_ij = scale * (q_i . k_j) - p_ij,
+ *   p_ij = min(strength * (max(|t_i - t_j| - window, 0) / falloff)^2, cap)
+ *          when q_seg[i] == output video and k_seg[j] == guide video, else 0,
+ *   o_i  = sum_j softmax_j(s_ij) v_j,   lse_i = ln sum_j exp(s_ij).
+ * The penalty is evaluated in registers per score tile; no rows x rows bias
+ * is ever formed. strength == 0 or cap == 0 gives plain attention (section 4).
+ * Queries are nq rows of q (with q_seg/q_t), keys nk rows of k and v (with
+ * k_seg/k_t); pass the same rows for self-attention or sub-ranges for
+ * partition calls.
+ * o_dtype: H3_DTYPE_F32 or H3_DTYPE_BF16 (bf16 rounding to nearest even).
+ * head_dim 64 or 128. fp32 inputs run a float32 path (no bf16 rounding);
+ * bf16 inputs use bf16 matrix cores with float32 accumulation.
+ * Workspace: attn_dense_tara_workspace(nk, heads, head_dim, dtype) bytes
+ * (0 for fp32); it holds a transposed copy of v used by the matrix cores.
+ * Errors: H3_EINVAL for null pointers, nq/nk/heads <= 0, non-finite knobs,
+ * strength/window/cap < 0, falloff <= 0, scale <= 0; H3_EUNSUPPORTED for a
+ * dtype or head_dim outside the lists above; H3_EWORKSPACE; H3_ELAUNCH.
+ */
+size_t attn_dense_tara_workspace(int nk, int heads, int head_dim, int dtype);
+int attn_dense_tara(const void* q, const void* k, const void* v, int dtype,
+                    int nq, int nk, int heads, int head_dim,
+                    const uint8_t* q_seg, const float* q_t,
+                    const uint8_t* k_seg, const float* k_t,
+                    float strength, float window, float falloff, float cap, float scale,
+                    void* o, int o_dtype, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Router plan (host only, no HIP call).
+ * From "H3 SLA Attention" ("How it works", "The inputs that matter", inputs
+ * table) and "H3 sparse-attention breakpoints" (the density is a fraction of
+ * the video KV tiles; text and audio are not reduced): the sequence is cut
+ * into nb = ceil(n / block_size) blocks (the last may be partial). A block is
+ * protected when it overlaps rows [0, protected_prefix_len) or holds any text
+ * or audio row; all other blocks are video tiles. The routed count is
+ *   k = min(n_video, max(1, ceil((1 - sparsity_ratio) * n_video - 1e-9))),
+ * k = n_video when sparsity_ratio == 0, and 0 when n_video == 0.
+ * seg_host: [n] host segment ids. Outputs may be NULL when not wanted.
+ * Errors: H3_EINVAL (seg_host null, n <= 0, protected_prefix_len not in
+ * [0, n], sparsity_ratio not in [0, 1) or non-finite); H3_EUNSUPPORTED
+ * (block_size != 64).
+ */
+int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, int block_size,
+                     double sparsity_ratio, int* nb, int* n_video, int* n_prot, int* k_sel);
+
+/*
+ * Pooled block router.
+ * From "H3 SLA Attention", "How it works": every query block is scored
+ * against every key block by one pooled Q/K product and keeps its top k video
+ * tiles. Per head: qbar_b, kbar_b = mean of the block's valid rows (float32
+ * sums in row order from +0.0, then a correctly rounded division by the row
+ * count); score(qb, kb) = sum over d = 0..head_dim-1 of fl32(qbar[d] *
+ * kbar[d]) added in order, no fused multiply-add, unscaled, over video tiles
+ * kb only; the k_sel highest scores are kept (ties to the lower block index,
+ * NaN last) and written in ascending block order. Every query block is
+ * routed, text and audio blocks included.
+ * tiles: device int32 [heads][ceil(n/64)][k_sel]; entries past the device's
+ *        video-tile count are -1.
+ * prot:  device int32 [n_prot] ascending protected block indices; n_prot is the
+ *        count from attn_router_plan on the same seg, and at most n_prot entries
+ *        are written.
+ * Workspace: attn_block_router_workspace(n, heads, head_dim, block_size).
+ * Errors: as attn_router_plan, plus H3_EINVAL for null q/k/seg, null tiles
+ * (k_sel > 0), null prot (n_prot > 0), k_sel < 0, k_sel > ceil(n/64) or
+ * n_prot < 0; H3_EUNSUPPORTED for dtype/head_dim or more than 14,000 blocks;
+ * H3_EWORKSPACE; H3_ELAUNCH.
+ */
+size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size);
+int attn_block_router(const void* q, const void* k, int dtype, int n, int heads, int head_dim,
+                      const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
+                      int32_t* tiles, int32_t* prot, int n_prot,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention over routed tiles.
+ * From "H3 SLA Attention", "How it works" and inputs table: query block qb of
+ * head h attends the keys of its protected blocks prot[0..n_prot) and its
+ * routed blocks tiles[h][qb][0..k_sel) (entries < 0 are skipped) and nothing
+ * else (a hard zero, no tail term). Inside those tiles the score is the dense
+ * TARA score of attn_dense_tara, so the penalty applies to routed guide tiles
+ * of output-video queries when strength > 0 and cap > 0.
+ * Workspace: attn_block_sparse_workspace(n, heads, head_dim, dtype) bytes.
+ * Errors: as attn_dense_tara, plus H3_EINVAL for k_sel < 0, n_prot < 0,
+ * n_prot + k_sel == 0, null tiles (k_sel > 0) or prot (n_prot > 0);
+ * H3_EUNSUPPORTED for block_size != 64.
+ */
+size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype);
+int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,
+                      int n, int heads, int head_dim,
+                      const uint8_t* seg, const float* t,
+                      float strength, float window, float falloff, float cap, float scale,
+                      int block_size, const int32_t* tiles, int k_sel,
+                      const int32_t* prot, int n_prot,
+                      void* o, int o_dtype, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stable LSE merge of one partition result into an accumulator, in place.
+ * From "Flash Partitions for H3 native temporal alignment", section 4:
+ *   adjusted_L = lse_i + log_w (+ log_w_rows[row][h] when non-NULL),
+ *   L = logaddexp(lse_acc, adjusted_L),
+ *   o_acc = exp(lse_acc - L) * o_acc + exp(adjusted_L - L) * o_i,
+ *   lse_acc = L.
+ * All float32 device buffers: o_acc, o_i [rows][heads][head_dim]; lse_acc,
+ * lse_i, log_w_rows [rows][heads]. Start an accumulator at o = 0 and
+ * lse = -inf; -inf merged with -inf stays -inf with o unchanged. A part whose
+ * adjusted normaliser is -inf (zero weight) is a no-op; log_w == -inf returns
+ * H3_OK without a launch.
+ * Errors: H3_EINVAL (null buffers, rows/heads <= 0, log_w NaN or +inf),
+ * H3_EUNSUPPORTED (head_dim not in {64,128}), H3_ELAUNCH.
+ */
+int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,
+                        float log_w, const float* log_w_rows, int rows, int heads, int head_dim,
+                        void* stream);
+
+/*
+ * Dense TARA attention through the positive-partition decomposition.
+ * From "Flash Partitions for H3 native temporal alignment", sections 3-4:
+ * exp(-p) = exp(-cap) + [exp(-p) - exp(-cap)]. Queries outside the output
+ * video get one ordinary attention call over every key. For output-video
+ * queries the library runs ordinary attention calls (with LSE) over: each
+ * run of non-guide keys (multiplier 1); each run of guide keys (multiplier
+ * exp(-cap)); and, per output frame f and guide frame g, the keys of g
+ * (multiplier exp(-cap) * expm1(cap - p(|t_f - t_g|)), omitted when zero);
+ * it merges them with partition_lse_merge. Frames are maximal runs of equal
+ * timestamp within a guide or output run. The result equals attn_dense_tara
+ * up to rounding order. Self-attention only (q, k, v share the n rows).
+ * seg_host/t_host: host copies of seg/t (used to plan the calls).
+ * Workspace: attn_dense_tara_via_workspace(seg_host, t_host, n, heads,
+ * head_dim, dtype) bytes. Errors: as attn_dense_tara.
+ */
+size_t attn_dense_tara_via_workspace(const uint8_t* seg_host, const float* t_host, int n,
+                                     int heads, int head_dim, int dtype);
+int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype,
+                        int n, int heads, int head_dim,
+                        const uint8_t* seg, const float* t,
+                        const uint8_t* seg_host, const float* t_host,
+                        float strength, float window, float falloff, float cap, float scale,
+                        void* o, int o_dtype, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

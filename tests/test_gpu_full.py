@@ -1,0 +1,107 @@
+"""GPU parity at the full 116,883-row x 56-head size, in the same launch
+configuration the benchmark times, on sampled outputs the oracle computes one
+by one: 3 heads x 8 fixed query blocks (segment boundaries and the 19-row tail)
+plus 4 seeded random blocks. Router tile lists are compared bit-exactly for the
+sampled heads in full."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_02_amd import api, workloads as W
+from gpu_common import compare, f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+HEADS = [0, 27, 55]
+FIXED_BLOCKS = [0, 113, 500, 962, 970, 977, 1400, 1826]
+
+
+def _blocks():
+    rng = np.random.default_rng(2024)
+    return sorted(set(FIXED_BLOCKS) | set(rng.integers(0, 1827, 4).tolist()))
+
+
+@pytest.fixture(scope="module")
+def full():
+    wl = W.FULL_SPARSE
+    t0 = time.time()
+    q, k, v = W.make_qkv(wl)
+    print(f"inputs generated in {time.time() - t0:.1f}s", flush=True)
+    seg, t = W.layout(wl)
+    dev = dict(q=to_device(q, "bf16"), k=to_device(k, "bf16"), v=to_device(v, "bf16"),
+               seg=torch.from_numpy(seg).cuda(), t=torch.from_numpy(t).cuda())
+    host = {n: f64(x[:, HEADS], "bf16") for n, x in (("q", q), ("k", k), ("v", v))}
+    host32 = {n: W.to_float32(x[:, HEADS], "bf16") for n, x in (("q", q), ("k", k))}
+    return wl, seg, t, dev, host, host32
+
+
+def _sample_rows(blocks, n):
+    return np.concatenate([np.arange(b * 64, min(n, b * 64 + 64)) for b in blocks])
+
+
+def _dense_ref(wl, seg, t, host, rows):
+    o, l = oracle.dense_tara(host["q"][rows], host["k"], host["v"], seg[rows], t[rows], seg, t,
+                             wl.tara, wl.scale)
+    return o, l
+
+
+def test_full_dense_direct_sampled(full):
+    wl, seg, t, dev, host, _ = full
+    print("dense direct 116883 x 56", flush=True)
+    o, lse = api.attn_dense_tara(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], dev["seg"],
+                                 dev["t"], *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(_blocks(), wl.n)
+    o_ref, l_ref = _dense_ref(wl, seg, t, host, rows)
+    ri = torch.from_numpy(rows).cuda()
+    compare(o[ri][:, HEADS], lse[ri][:, HEADS], o_ref, l_ref, "bf16", "full dense direct")
+
+
+def test_full_dense_via_sampled(full):
+    wl, seg, t, dev, host, _ = full
+    print("dense via partitions 116883 x 56", flush=True)
+    o, lse = api.attn_dense_tara_via(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], seg, t,
+                                     *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(_blocks(), wl.n)
+    o_ref, l_ref = _dense_ref(wl, seg, t, host, rows)
+    ri = torch.from_numpy(rows).cuda()
+    compare(o[ri][:, HEADS], lse[ri][:, HEADS], o_ref, l_ref, "bf16", "full dense via")
+
+
+@pytest.mark.parametrize("sparsity", [0.90, 0.50])
+def test_full_router_and_sparse_sampled(full, sparsity):
+    wl, seg, t, dev, host, host32 = full
+    plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
+    assert plan["n_prot"] == 130 and plan["n_video"] == 1697
+    print(f"router + sparse s={sparsity} k={plan['k_sel']}", flush=True)
+    tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
+                                        plan["k_sel"], plan["n_prot"])
+    o, lse = api.attn_block_sparse(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], tiles,
+                                   prot, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    tl = tiles.cpu().numpy()[HEADS]
+    pr = prot.cpu().numpy()
+    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, 64, sparsity)
+    assert np.array_equal(pr, prot_ref)
+    for j in range(len(HEADS)):
+        ref = oracle.route_head(host32["q"][:, j], host32["k"][:, j], seg,
+                                wl.protected_prefix_len, 64, plan["k_sel"])
+        mism = int(np.sum(np.any(tl[j] != ref, axis=1)))
+        print(f"head {HEADS[j]}: {mism} mismatching tile lists of 1827", flush=True)
+        assert mism == 0
+    blocks = _blocks()
+    ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64, pr,
+                              tl, heads=range(len(HEADS)), qblocks=blocks)
+    og, lg, orf, lrf = [], [], [], []
+    for (j, qb), (ob, lb) in ref.items():
+        lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
+        og.append(o[lo:hi, HEADS[j]])
+        lg.append(lse[lo:hi, HEADS[j]])
+        orf.append(ob)
+        lrf.append(lb)
+    compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
+            f"full sparse s={sparsity}")

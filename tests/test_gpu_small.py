@@ -1,0 +1,319 @@
+"""GPU parity at sizes the oracle finishes in seconds: every output element of
+the HIP path against the float64 oracle, plus edge cases (ragged tails, tiles
+straddling frames and segments, head_dim 64, sub-range calls, ties)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_02_amd import api, workloads as W
+from gpu_common import compare, f64, layout_device, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _dense_case(wl, o_dtype=None, params=None):
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, wl.dtype) for x in (q, k, v))
+    p = params or wl.tara
+    od = {"f32": torch.float32, "bf16": torch.bfloat16}[o_dtype or wl.dtype]
+    print(f"case {wl.name} n={wl.n} H={wl.heads} d={wl.head_dim} params={p} o={od}", flush=True)
+    o, lse = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *p, scale=wl.scale,
+                                 o_dtype=od)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q, wl.dtype), f64(k, wl.dtype), f64(v, wl.dtype), seg, t,
+                                     seg, t, p, wl.scale)
+    return o, lse, o_ref, l_ref
+
+
+def test_dense_tiny_fp32():
+    """304 rows, 1 head, d 64, float32, default penalty."""
+    wl = W.TINY_DENSE
+    o, lse, o_ref, l_ref = _dense_case(wl)
+    compare(o, lse, o_ref, l_ref, "f32", wl.name)
+
+
+def test_dense_mid_bf16():
+    """6,800 rows, 24 heads, d 128, bf16, default penalty, every output."""
+    wl = W.MID_DENSE
+    o, lse, o_ref, l_ref = _dense_case(wl)
+    compare(o, lse, o_ref, l_ref, "bf16", wl.name)
+
+
+def _ragged(d, dtype, seed, strength=2.0, heads=3):
+    # frames of 37 and 45 rows: tiles straddle frames and segments; n not a multiple of 64
+    return W.custom(f"ragged_d{d}_{dtype}_{seed}",
+                    [W.Span(W.SEG_TEXT, 29), W.Span(W.SEG_GUIDE, 7 * 37, 7),
+                     W.Span(W.SEG_AUDIO, 51), W.Span(W.SEG_OUTPUT, 7 * 45, 7),
+                     W.Span(W.SEG_TEXT, 13)],
+                    heads=heads, head_dim=d, dtype=dtype, seed_index=seed, frame_weight=0.5,
+                    strength=strength)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dense_ragged_layouts(d, dtype):
+    wl = _ragged(d, dtype, 40 + d)
+    assert wl.n % 64 != 0
+    o, lse, o_ref, l_ref = _dense_case(wl)
+    compare(o, lse, o_ref, l_ref, dtype, wl.name)
+
+
+@pytest.mark.parametrize("params", [(0.0, 0.2, 0.25, 6.0), (2.0, 0.2, 0.25, 0.0),
+                                    (8.0, 0.05, 0.1, 12.0), (0.7, 0.0, 0.5, 2.0)])
+def test_dense_penalty_knobs_bf16(params):
+    """Off-switches and non-default knobs, including a cap large enough to matter."""
+    wl = _ragged(128, "bf16", 60, heads=2)
+    o, lse, o_ref, l_ref = _dense_case(wl, params=params)
+    compare(o, lse, o_ref, l_ref, "bf16", f"{wl.name}:{params}")
+
+
+def test_dense_bf16_with_fp32_output():
+    wl = _ragged(128, "bf16", 61, heads=2)
+    o, lse, o_ref, l_ref = _dense_case(wl, o_dtype="f32")
+    assert o.dtype == torch.float32
+    compare(o, lse, o_ref, l_ref, "bf16", wl.name + ":o32")
+
+
+def test_dense_single_row_and_tiny_key_sets():
+    """nq = 1 and nk = 1..3 (one partial tile)."""
+    wl = _ragged(64, "bf16", 62, heads=2)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    for (qa, qb, ka, kb) in [(300, 301, 0, 1), (300, 301, 40, 43), (0, 64, 330, 331),
+                             (333, 400, 29, 30)]:
+        o, lse = api.attn_dense_tara(qd[qa:qb], kd[ka:kb], vd[ka:kb], seg_d[qa:qb], t_d[qa:qb],
+                                     seg_d[ka:kb], t_d[ka:kb], *wl.tara, scale=wl.scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.dense_tara(f64(q[qa:qb], "bf16"), f64(k[ka:kb], "bf16"),
+                                         f64(v[ka:kb], "bf16"), seg[qa:qb], t[qa:qb],
+                                         seg[ka:kb], t[ka:kb], wl.tara, wl.scale)
+        compare(o, lse, o_ref, l_ref, "bf16", f"sub {qa}:{qb} x {ka}:{kb}")
+
+
+def test_dense_subrange_partition_call():
+    """Queries of one output frame against the guide run only (nq != nk, offsets)."""
+    wl = W.MID_DENSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl, heads=range(4))
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    qa, qb, ka, kb = 3728 + 2 * 256, 3728 + 3 * 256, 256, 3328
+    o, lse = api.attn_dense_tara(qd[qa:qb], kd[ka:kb], vd[ka:kb], seg_d[qa:qb], t_d[qa:qb],
+                                 seg_d[ka:kb], t_d[ka:kb], *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q[qa:qb], "bf16"), f64(k[ka:kb], "bf16"),
+                                     f64(v[ka:kb], "bf16"), seg[qa:qb], t[qa:qb], seg[ka:kb],
+                                     t[ka:kb], wl.tara, wl.scale)
+    compare(o, lse, o_ref, l_ref, "bf16", "frame2 x guide")
+
+
+def test_dense_is_deterministic():
+    wl = _ragged(128, "bf16", 63, heads=2)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o1, l1 = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *wl.tara)
+    o2, l2 = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *wl.tara)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------- router
+
+def _route_oracle(wl, q, k, seg, k_sel, heads):
+    return np.stack([oracle.route_head(W.to_float32(q[:, j], wl.dtype),
+                                       W.to_float32(k[:, j], wl.dtype), seg,
+                                       wl.protected_prefix_len, 64, k_sel) for j in heads])
+
+
+def test_router_mid_bit_exact():
+    """31,552 rows, 24 heads, s = 0.85: every tile list of every head and block."""
+    wl = W.MID_SPARSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.85)
+    assert (plan["nb"], plan["n_prot"], plan["n_video"], plan["k_sel"]) == (493, 15, 478, 72)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, wl.protected_prefix_len, plan["k_sel"],
+                                        plan["n_prot"])
+    torch.cuda.synchronize()
+    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, 64, 0.85)
+    assert np.array_equal(prot.cpu().numpy(), prot_ref)
+    ref = _route_oracle(wl, q, k, seg, plan["k_sel"], range(wl.heads))
+    got = tiles.cpu().numpy()
+    mism = int(np.sum(np.any(got != ref, axis=2)))
+    print(f"router mismatching (head, block) lists: {mism} of {got.shape[0] * got.shape[1]}")
+    assert mism == 0
+
+
+def test_router_edges_ties_ragged_and_padding():
+    """Ragged last block, duplicated rows (exactly tied pooled scores), k_sel above
+    the video-tile count (padded with -1), fp32 and bf16."""
+    for dtype in ("bf16", "f32"):
+        wl = W.custom(f"rt_{dtype}", [W.Span(W.SEG_TEXT, 70), W.Span(W.SEG_GUIDE, 6 * 100, 6),
+                                      W.Span(W.SEG_AUDIO, 20), W.Span(W.SEG_OUTPUT, 6 * 100, 6)],
+                      heads=3, head_dim=64, dtype=dtype, seed_index=70, frame_weight=0.7,
+                      protected_prefix_len=70)
+        seg, t, seg_d, t_d = layout_device(wl)
+        q, k, v = W.make_qkv(wl)
+        k[192:256] = k[128:192]          # video blocks 2, 3 and 5 hold identical key rows
+        k[320:384] = k[128:192]
+        qd, kd = to_device(q, dtype), to_device(k, dtype)
+        nb, prot_ref, vid, _ = oracle.router_plan(seg, 70, 64, 0.0)
+        for k_sel in (1, 3, len(vid), nb):
+            tiles, prot = api.attn_block_router(qd, kd, seg_d, 70, k_sel, len(prot_ref))
+            torch.cuda.synchronize()
+            got = tiles.cpu().numpy()
+            kk = min(k_sel, len(vid))
+            ref = _route_oracle(wl, q, k, seg, kk, range(3))
+            assert np.array_equal(got[:, :, :kk], ref), (dtype, k_sel)
+            assert np.all(got[:, :, kk:] == -1)
+            assert np.array_equal(prot.cpu().numpy(), prot_ref)
+
+
+# ------------------------------------------------------------------- sparse
+
+def test_sparse_mid_sampled_blocks():
+    """31,552 rows, s = 0.85, no penalty: routed tiles from the GPU router (checked
+    bit-exact first), outputs of sampled (head, block) pairs against the oracle."""
+    wl = W.MID_SPARSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.85)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, wl.protected_prefix_len, plan["k_sel"],
+                                        plan["n_prot"])
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
+                                   scale=wl.scale)
+    torch.cuda.synchronize()
+    tl = tiles.cpu().numpy()
+    pr = prot.cpu().numpy()
+    heads = [0, 11, 23]
+    ref_tiles = _route_oracle(wl, q, k, seg, plan["k_sel"], heads)
+    assert np.array_equal(tl[heads], ref_tiles)
+    rng = np.random.default_rng(3)
+    blocks = sorted(set([0, 1, 14, 15, 200, 253, 254, 492]) | set(rng.integers(0, 493, 12).tolist()))
+    q64, k64, v64 = (f64(x[:, heads], "bf16") for x in (q, k, v))
+    ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 64, pr,
+                              tl[heads], heads=range(3), qblocks=blocks)
+    og, lg, orf, lrf = [], [], [], []
+    for (j, qb), (ob, lb) in ref.items():
+        lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
+        og.append(o[lo:hi, heads[j]])
+        lg.append(lse[lo:hi, heads[j]])
+        orf.append(ob)
+        lrf.append(lb)
+    compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
+            "sparse mid")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sparse_every_tile_equals_dense(dtype):
+    """Sparsity 0 (every video tile routed) reproduces dense TARA."""
+    wl = _ragged(128 if dtype == "bf16" else 64, dtype, 80)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    plan = api.router_plan(seg, 0, 0.0)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, 0, plan["k_sel"], plan["n_prot"])
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
+                                   scale=wl.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, seg, t,
+                                     wl.tara, wl.scale)
+    compare(o, lse, o_ref, l_ref, dtype, f"sparse s=0 {dtype}")
+
+
+@pytest.mark.parametrize("sparsity", [0.5, 0.9])
+def test_sparse_with_penalty_small(sparsity):
+    """Routed guide tiles carry the TARA penalty; every output against the oracle."""
+    wl = W.custom("sp_pen", [W.Span(W.SEG_TEXT, 100), W.Span(W.SEG_GUIDE, 8 * 130, 8),
+                             W.Span(W.SEG_AUDIO, 60), W.Span(W.SEG_OUTPUT, 8 * 130, 8)],
+                  heads=4, head_dim=128, dtype="bf16", seed_index=90, frame_weight=0.7,
+                  protected_prefix_len=100)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, 100, sparsity)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, 100, plan["k_sel"], plan["n_prot"])
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
+                                   scale=wl.scale)
+    torch.cuda.synchronize()
+    tl = tiles.cpu().numpy()
+    assert np.array_equal(tl, _route_oracle(wl, q, k, seg, plan["k_sel"], range(4)))
+    ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
+                              wl.scale, 64, prot.cpu().numpy(), tl)
+    o_ref = np.zeros((wl.n, 4, 128))
+    l_ref = np.zeros((wl.n, 4))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * 64:qb * 64 + len(ob), h] = ob
+        l_ref[qb * 64:qb * 64 + len(ob), h] = lb
+    compare(o, lse, o_ref, l_ref, "bf16", f"sparse pen s={sparsity}")
+
+
+# ------------------------------------------------------------------- merge
+
+def test_lse_merge_matches_oracle():
+    """Successive merges of random partials, including -inf rows and weights."""
+    rng = np.random.default_rng(9)
+    rows, H, D = 300, 3, 128
+    parts = []
+    for i in range(4):
+        o = rng.standard_normal((rows, H, D))
+        l = rng.standard_normal((rows, H)) * 3
+        l[rng.random((rows, H)) < 0.2] = -np.inf
+        parts.append((o, l, [0.0, -6.0, math.log(0.2755), -2.5][i]))
+    o_ref, l_ref = oracle.lse_merge(parts)
+    acc = torch.zeros((rows, H, D), dtype=torch.float32, device="cuda")
+    acc_l = torch.full((rows, H), -float("inf"), dtype=torch.float32, device="cuda")
+    for o, l, w in parts:
+        api.partition_lse_merge(acc, acc_l, torch.tensor(o, dtype=torch.float32, device="cuda"),
+                                torch.tensor(l, dtype=torch.float32, device="cuda"), log_w=w)
+    torch.cuda.synchronize()
+    o32 = np.stack([p[0] for p in parts]).astype(np.float32).astype(np.float64)
+    assert np.all(np.isfinite(o32))
+    got_o = acc.cpu().numpy()
+    got_l = acc_l.cpu().numpy()
+    both_inf = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(got_l), both_inf)
+    assert np.all(got_o[both_inf] == 0.0)
+    assert np.max(np.abs(got_o - o_ref)) < 1e-5
+    assert np.max(np.abs(got_l[~both_inf] - l_ref[~both_inf])) < 1e-5
+
+
+def test_lse_merge_per_row_weights_and_noop():
+    rng = np.random.default_rng(10)
+    rows, H, D = 64, 2, 64
+    o1, o2 = rng.standard_normal((2, rows, H, D))
+    l1, l2 = rng.standard_normal((2, rows, H))
+    lw = rng.standard_normal((rows, H))
+    o_ref, l_ref = oracle.lse_merge([(o1, l1, 0.0), (o2, l2, lw)])
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+    acc, accl = t(o1), t(l1)
+    api.partition_lse_merge(acc, accl, t(o2), t(l2), log_w=0.0, log_w_rows=t(lw))
+    api.partition_lse_merge(acc, accl, t(o2) * 1e9, t(l2), log_w=-float("inf"))  # no-op
+    torch.cuda.synchronize()
+    assert np.max(np.abs(acc.cpu().numpy() - o_ref)) < 1e-5
+    assert np.max(np.abs(accl.cpu().numpy() - l_ref)) < 1e-5
+
+
+# ------------------------------------------------------------------- via
+
+@pytest.mark.parametrize("wl", [W.TINY_DENSE, W.MID_DENSE], ids=lambda w: w.name)
+def test_via_partitions_match_oracle_and_direct(wl):
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, wl.dtype) for x in (q, k, v))
+    o, lse = api.attn_dense_tara_via(qd, kd, vd, seg_d, t_d, seg, t, *wl.tara, scale=wl.scale)
+    od, ld = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q, wl.dtype), f64(k, wl.dtype), f64(v, wl.dtype), seg,
+                                     t, seg, t, wl.tara, wl.scale)
+    compare(o, lse, o_ref, l_ref, wl.dtype, wl.name + " via")
+    diff = float((o.float() - od.float()).abs().max())
+    print(f"via vs direct max diff {diff:.3e}")
+    assert diff <= (2e-2 if wl.dtype == "bf16" else 1e-4)
