@@ -1,0 +1,290 @@
+"""Benchmark of the TARA dense / block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over the full-scale packed sequence
+(116,883 rows x 56 heads x d 128, bf16, inputs resident in HBM):
+  1. dense TARA attention, one direct call (attn_dense_tara);
+  2. block-sparse attention at sparsity 0.90: router (attn_block_router) +
+     sparse attention (attn_block_sparse) with the TARA penalty on routed
+     guide tiles;
+  3. dense TARA through the positive-partition decomposition with LSE merges
+     (attn_dense_tara_via).
+Each of the three produces a full attention output, i.e. 4*N^2*d*H = 391.71
+dense-equivalent TFLOP; ``value`` is 3 x 391.71 TFLOP / step time. Per-call
+ms, dense-equivalent TFLOP/s and fraction of the bf16 MFMA peak are reported
+beside it, with a sparsity sweep, the roofline of the dominant kernel (the
+dense TARA attention kernel) and the float64 CPU oracle timed on a sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms/call + dense-equiv TFLOP/s (%MFMA peak), 116,883 rows x 56 heads, 1 GPU"
+DENSE_KERNEL = "attn_bf16_kernel<128, 4, 1, false, true>"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_dense_tara_116883x56_pmc.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "block_sparse_attention_02_amd", "csrc", "attn_bf16.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--sparsity", type=float, default=0.90)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["all", "dense", "sparse", "via"], default="all",
+                    help="profiling aid: run one row of the step only (the JSON line then "
+                         "covers that row)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, q, k, v, seg, t):
+    """The float64 oracle on a bounded sample of the same workload."""
+    import oracle
+    from block_sparse_attention_02_amd import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            threads = min(threads, int(os.environ[var]))
+            break
+    heads = [0, 27, 55]
+    blocks = [0, 500, 970, 1400]
+    rows = np.concatenate([np.arange(b * 64, min(wl.n, b * 64 + 64)) for b in blocks])
+    q64 = W.to_float64(q[rows][:, heads], "bf16")
+    k64 = W.to_float64(k[:, heads], "bf16")
+    v64 = W.to_float64(v[:, heads], "bf16")
+    t0 = time.perf_counter()
+    oracle.dense_tara(q64, k64, v64, seg[rows], t[rows], seg, t, wl.tara, wl.scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(rows) * wl.n * wl.head_dim * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 dense TARA oracle, {len(rows)} query rows x {wl.n} keys x "
+                      f"{len(heads)} heads ({flops / 1e12:.3f} dense TFLOP) in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the attention is "
+                                   "sharded by head across GPUs only by design (see DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_02_amd import api, workloads as W
+
+    torch.cuda.set_device(0)
+    wl = W.FULL_SPARSE
+    N, H, D = wl.n, wl.heads, wl.head_dim
+    dense_flop = 4.0 * N * N * D * H
+    t0 = time.time()
+    q, k, v = W.make_qkv(wl)
+    seg, t = W.layout(wl)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    segd, td = torch.from_numpy(seg).cuda(), torch.from_numpy(t).cuda()
+    scale = wl.scale
+    tara = wl.tara
+    plan = api.router_plan(seg, wl.protected_prefix_len, args.sparsity)
+    k_sel, n_prot, nb = plan["k_sel"], plan["n_prot"], plan["nb"]
+    kept = (n_prot + k_sel) / nb
+
+    # every buffer allocated up front: the timed region only launches kernels
+    o_dense = torch.empty_like(qd)
+    l_dense = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    ws_dense = torch.empty(api.dense_tara_workspace_bytes(N, H, D, 1), dtype=torch.uint8,
+                           device="cuda")
+    tiles = torch.empty((H, nb, k_sel), dtype=torch.int32, device="cuda")
+    prot = torch.empty((n_prot,), dtype=torch.int32, device="cuda")
+    ws_router = torch.empty(api.router_workspace_bytes(N, H, D), dtype=torch.uint8, device="cuda")
+    o_sparse = torch.empty_like(qd)
+    l_sparse = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    o_via = torch.empty_like(qd)
+    l_via = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    ws_via = torch.empty(api.via_workspace_bytes(seg, t, H, D, 1), dtype=torch.uint8,
+                         device="cuda")
+
+    stream = torch.cuda.current_stream()
+    rows = {"dense": [], "router": [], "sparse": [], "via": []}
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record):
+        marks = []
+        if args.only in ("all", "dense"):
+            a = ev()
+            api.attn_dense_tara(qd, kd, vd, segd, td, segd, td, *tara, scale=scale, o=o_dense,
+                                lse=l_dense, ws=ws_dense)
+            marks.append(("dense", a, ev()))
+        if args.only in ("all", "sparse"):
+            a = ev()
+            api.attn_block_router(qd, kd, segd, wl.protected_prefix_len, k_sel, n_prot,
+                                  tiles=tiles, prot=prot, ws=ws_router)
+            b = ev()
+            api.attn_block_sparse(qd, kd, vd, segd, td, tiles, prot, *tara, scale=scale,
+                                  o=o_sparse, lse=l_sparse, ws=ws_dense)
+            marks.append(("router", a, b))
+            marks.append(("sparse", b, ev()))
+        if args.only in ("all", "via"):
+            a = ev()
+            api.attn_dense_tara_via(qd, kd, vd, segd, td, seg, t, *tara, scale=scale, o=o_via,
+                                    lse=l_via, ws=ws_via)
+            marks.append(("via", a, ev()))
+        return marks
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        print(f"# warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    all_marks = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        all_marks.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    for marks in all_marks:
+        for name, a, b in marks:
+            rows[name].append(a.elapsed_time(b))
+    print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
+
+    ms_step = wall * 1e3 / args.steps
+    n_calls = {"all": 3, "dense": 1, "sparse": 1, "via": 1}[args.only]
+    value = n_calls * dense_flop / (ms_step * 1e-3) / 1e12
+
+    def summary(name):
+        xs = rows[name]
+        if not xs:
+            return None
+        med = float(np.median(xs))
+        return {"ms": med, "ms_mean": float(np.mean(xs)), "n": len(xs)}
+
+    calls = {}
+    d = summary("dense")
+    if d:
+        tf = dense_flop / (d["ms"] * 1e-3) / 1e12
+        calls["dense_tara"] = dict(d, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
+    r, s = summary("router"), summary("sparse")
+    if r and s:
+        tot = r["ms"] + s["ms"]
+        tf = dense_flop / (tot * 1e-3) / 1e12
+        calls["block_sparse"] = {
+            "sparsity": args.sparsity, "k_sel": k_sel, "n_prot": n_prot, "kept_frac": kept,
+            "router_ms": r["ms"], "sparse_ms": s["ms"], "ms": tot,
+            "dense_equiv_tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS,
+            "executed_tflops": kept * dense_flop / (s["ms"] * 1e-3) / 1e12,
+            "speedup_vs_dense": (d["ms"] / tot) if d else None,
+            "target_speedup": 0.8 / kept,
+        }
+    vi = summary("via")
+    if vi:
+        tf = dense_flop / (vi["ms"] * 1e-3) / 1e12
+        calls["dense_tara_via"] = dict(vi, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
+
+    sweep = {}
+    if not args.no_sweep and args.only in ("all", "sparse"):
+        for sp in wl.sparsities:
+            pl = api.router_plan(seg, wl.protected_prefix_len, sp)
+            tl = torch.empty((H, nb, pl["k_sel"]), dtype=torch.int32, device="cuda")
+            rt, st = [], []
+            for rep in range(4):
+                a = ev()
+                api.attn_block_router(qd, kd, segd, wl.protected_prefix_len, pl["k_sel"], n_prot,
+                                      tiles=tl, prot=prot, ws=ws_router)
+                b = ev()
+                api.attn_block_sparse(qd, kd, vd, segd, td, tl, prot, *tara, scale=scale,
+                                      o=o_sparse, lse=l_sparse, ws=ws_dense)
+                c = ev()
+                torch.cuda.synchronize()
+                if rep:
+                    rt.append(a.elapsed_time(b))
+                    st.append(b.elapsed_time(c))
+            kf = (n_prot + pl["k_sel"]) / nb
+            tot = float(np.median(rt) + np.median(st))
+            sweep[f"{sp:.2f}"] = {"k_sel": pl["k_sel"], "kept_frac": kf,
+                                  "router_ms": float(np.median(rt)),
+                                  "sparse_ms": float(np.median(st)),
+                                  "speedup_vs_dense": (d["ms"] / tot) if d else None,
+                                  "ideal_speedup": 1.0 / kf}
+        print("# sweep done", file=sys.stderr, flush=True)
+
+    roofline = None
+    if d:
+        traffic = None
+        if os.path.exists(PMC_SUMMARY):
+            with open(PMC_SUMMARY) as f:
+                pmc = json.load(f)
+            if pmc.get("source_hash") == kernel_source_hash():
+                traffic = pmc.get("hbm_bytes_per_launch")
+        achieved = dense_flop / (d["ms_mean"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                    "kernel": DENSE_KERNEL,
+                    "per_launch": "4*N^2*d*H = 391.71 TFLOP (116,883 x 116,883 x 128 x 56)",
+                    "timing": "HIP events on the launch stream around each attn_dense_tara call "
+                              "(includes the v-transpose pre-pass), mean over timed steps"}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, q, k, v, seg, t)
+        print("# cpu baseline done", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "packed sequence 116,883 rows x 56 heads x d 128 bf16: dense "
+                               "TARA direct + router/block-sparse s=%.2f + partition path"
+                               % args.sparsity,
+                   "rows": N, "heads": H, "head_dim": D, "block_size": 64,
+                   "sparsity": args.sparsity, "step_rows": args.only,
+                   "tara": {"strength": tara[0], "window": tara[1], "falloff": tara[2],
+                            "cap": tara[3]}},
+        "calls": calls,
+        "sparsity_sweep": sweep,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -33,9 +33,15 @@ def _sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# The router's pooled scores are defined as separately rounded products and sums,
+# so no multiply-add may be contracted anywhere in that file.
+PER_FILE = {"router.hip": ["-ffp-contract=off"]}
+
+
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -16,10 +16,13 @@
 // lane holds one query column; softmax row reductions stay in registers plus one
 // exchange between lane halves.
 // K and V^T tiles are double-buffered in LDS with an XOR swizzle on 16-byte chunks
-// (bank-conflict-free operand reads), prefetched through registers one tile ahead.
+// (bank-conflict-free operand reads) and loaded one tile ahead straight from global
+// memory into LDS (global_load_lds_dwordx4), so the loads hold no registers.
 // V^T comes from a transposed copy of v whose keys are permuted within 16-key groups
 // (bits 2 and 3 of the key index swapped) so that the probability registers produced by
 // the first product are directly the B operand of the second.
+#include <type_traits>
+
 #include "h3_internal.h"
 
 namespace h3 {
@@ -27,6 +30,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -37,6 +41,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running maxima are only raised when a tile exceeds them by more than this (log2
 // units); probabilities then stay below 2^8 and most tiles skip the O rescale.
 constexpr float kLazyRescale = 8.0f;
+// Buffer descriptor word 3 for raw 32-bit-format loads on CDNA (out-of-range reads
+// return zero).
+constexpr int kBufferFlags = 0x00020000;
 
 // Position of key `key` inside its 16-key group of the transposed v copy.
 __host__ __device__ constexpr int key_pos(int key) {
@@ -46,6 +53,16 @@ __host__ __device__ constexpr int key_pos(int key) {
 // Lanes l and l^32 hold the two key halves of the same query column.
 __device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// One 16-byte chunk per lane from a raw buffer [base, base + nbytes) straight into LDS
+// at lds + 16 * lane (the LDS address is wave-uniform); out-of-range lanes read zero.
+__device__ __forceinline__ void buffer_to_lds16(const void* base, int nbytes, void* lds,
+                                                uint32_t voffset) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, 0);
+}
 
 __device__ __forceinline__ float tara_pen(float dt, float window, float inv_falloff,
                                           float strength, float cap) {
@@ -99,16 +116,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NS = KW / 16;         // k-steps of the PV product
   constexpr int DK = D / 16;          // k-steps of the QK product
   constexpr int DT = D / 32;          // 32-row output tiles (over d)
-  constexpr int KCH = 64 * D / 8;     // 16-byte chunks per K tile
-  constexpr int VCH = D * 8;          // 16-byte chunks per V^T tile
-  constexpr int KPT = KCH / 256;
-  constexpr int VPT = VCH / 256;
-  constexpr int CPR = D / 8;          // 16-byte chunks per K row
+  constexpr int TILE_ELEMS = 64 * D;  // bf16 elements of one K (or V^T) tile
+  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / 4;  // 1 KB wave loads per wave
+  constexpr int KROW_BYTES = D * 2;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * 64];
-  __shared__ uint8_t kseg_s[2][64];
-  __shared__ float kt_s[2][64];
+  // Two stages, each its own LDS object so the compiler can tell the stage being
+  // read from the stage being filled by the direct-to-LDS loads.
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[TILE_ELEMS];
+  __shared__ uint8_t kseg0[64], kseg1[64];
+  __shared__ float kt0[64], kt1[64];
   __shared__ int info_s[2];     // bit0 any guide key, bit1 all keys guide of one frame,
                                 // bit2 all 64 keys valid, bit3 tile skipped
   __shared__ float tuni_s[2];
@@ -153,59 +172,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   } else {
     ntiles = nkb;
   }
-  auto tile_of = [&](int i) -> int {
-    if (!SPARSE) return i;
-    return i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
+  auto tile_of = [&](int i) -> int __attribute__((always_inline)) {
+    int kb = i;
+    if (SPARSE) kb = i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
+    return __builtin_amdgcn_readfirstlane(kb);
   };
 
-  u32x4 kreg[KPT];
-  u32x4 vreg[VPT];
+  // ---- tile loads: K and V^T straight into LDS with buffer loads (one 16-byte chunk per
+  // lane per instruction, 1 KB per wave instruction). Each lane's byte offset inside a
+  // tile is fixed, so it is computed once; the tile base lives in a scalar descriptor.
+  // K rows past the end of the sequence fall outside the descriptor and are masked.
+  uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int off = (wave * DMA_PER_WAVE + i) * 1024 + lane * 16;  // byte offset in tile
+    const int r = off / KROW_BYTES, pc = (off % KROW_BYTES) / 16;    // key row, chunk
+    koff[i] = (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
+    const int d = off / 128, vc = (off % 128) / 16;                  // V^T row, chunk
+    voff[i] = (uint32_t)d * (uint32_t)(a.nkp * 2) + (uint32_t)((vc ^ (d & 7)) * 16);
+  }
+  auto dma = [&](int kb, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    const int k0 = kb * 64;
+    const int rows = min(64, a.nk - k0);
+    const void* kbase = kp + ((int64_t)k0 * H + h) * D;
+    const int kbytes = (rows - 1) * H * D * 2 + D * 2;
+    const void* vbase = vtp + (int64_t)h * D * a.nkp + k0;
+    const int vbytes = (D - 1) * a.nkp * 2 + 128;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      buffer_to_lds16(kbase, kbytes, kdst + (wave * DMA_PER_WAVE + i) * 512, koff[i]);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      buffer_to_lds16(vbase, vbytes, vdst + (wave * DMA_PER_WAVE + i) * 512, voff[i]);
+  };
   uint32_t sreg = kSegInvalid;
   float treg = 0.f;
-
-  auto gload = [&](int kb) {
-    if (kb >= 0 && kb < nkb) {
-      const int k0 = kb * 64;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int c = tid + i * 256;
-        const int r = c / CPR, ch = c % CPR;
-        const int key = min(k0 + r, a.nk - 1);  // ragged tail: clamped, masked later
-        kreg[i] = *(const u32x4*)(kp + ((int64_t)key * H + h) * D + ch * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int c = tid + i * 256;
-        const int d = c >> 3, ch = c & 7;
-        vreg[i] = *(const u32x4*)(vtp + ((int64_t)h * D + d) * a.nkp + k0 + ch * 8);
-      }
-      if (tid < 64) {
-        const int key = k0 + tid;
-        const bool kv = key < a.nk;
-        sreg = kv ? (uint32_t)a.k_seg[key] : (uint32_t)kSegInvalid;
-        treg = kv ? a.k_t[key] : 0.f;
-      }
-    } else {
-      if (tid < 64) { sreg = kSegInvalid; treg = 0.f; }
+  auto small_load = [&](int kb) __attribute__((always_inline)) {
+    if (tid < 64) {
+      const int key = kb * 64 + tid;
+      const bool kv = kb >= 0 && kb < nkb && key < a.nk;
+      sreg = kv ? (uint32_t)a.k_seg[key] : (uint32_t)kSegInvalid;
+      treg = kv ? a.k_t[key] : 0.f;
     }
   };
-
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / CPR, ch = c % CPR;
-      *(u32x4*)&ks[st][r * D + ((ch ^ (r & 7)) * 8)] = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * 256;
-      const int d = c >> 3, ch = c & 7;
-      *(u32x4*)&vs[st][d * 64 + ((ch ^ (d & 7)) * 8)] = vreg[i];
-    }
+  auto small_store = [&](uint8_t* sg, float* tt, int st) __attribute__((always_inline)) {
     if (tid < 64) {
-      kseg_s[st][tid] = (uint8_t)sreg;
-      kt_s[st][tid] = treg;
+      sg[tid] = (uint8_t)sreg;
+      tt[tid] = treg;
       const uint64_t g = __ballot(sreg == (uint32_t)kSegGuide);
       const uint64_t valid = __ballot(sreg != (uint32_t)kSegInvalid);
       const float t0 = __shfl(treg, 0);
@@ -221,6 +234,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
+  auto prefetch = [&](int i, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    const int kb = tile_of(i);
+    if (kb >= 0 && kb < nkb) dma(kb, kdst, vdst);
+    small_load(kb);
+  };
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -230,129 +248,142 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (ntiles > 0) {
-    gload(tile_of(0));
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(tile_of(it + 1));
-    const int info = __builtin_amdgcn_readfirstlane(info_s[st]);
-    if (!(info & 8)) {
-      // ---- S^T = K Q^T (keys as rows, this wave's 32 queries as columns)
-      f32x16 sacc[NT];
+  // ---- one tile: S^T = K Q^T, scores with the penalty, online softmax, O^T += V^T P^T.
+  // GENERAL handles masked keys and per-key penalties; the fast body covers tiles
+  // whose penalty is one scalar per query (or zero).
+  auto tile_body = [&](auto general_tag, const uint16_t* kst, const uint16_t* vst,
+                       const uint8_t* ksg, const float* ktt, bool uniform_guide,
+                       float tuni) __attribute__((always_inline)) {
+    constexpr bool GENERAL = decltype(general_tag)::value;
+    f32x16 sacc[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DK; ++s) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        const int kr = kh * KW + 32 * c + l32;
+        const bf16x8 ka = *(const bf16x8*)&kst[kr * D + (((2 * s + hh) ^ (kr & 7)) * 8)];
+        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
+      }
+    }
+    float cc = c_log2, bb = 0.f, tmax;
+    if (!GENERAL) {
+      if (PEN && uniform_guide && q_out) {
+        // every key is a guide row of one frame: one penalty per output query row
+        bb = -tara_pen(fabsf(qt - tuni), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
-      const uint16_t* kst = ks[st];
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[c][r], sacc[c][r + 1]));
+      tmax = mx * cc + bb;
+    } else {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < DK; ++s) {
+      for (int c = 0; c < NT; ++c) {
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const int kr = kh * KW + 32 * c + l32;
-          const bf16x8 ka = *(const bf16x8*)&kst[kr * D + (((2 * s + hh) ^ (kr & 7)) * 8)];
-          sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
-        }
-      }
-
-      // ---- scores in log2 units: x = s*scale*log2e - pen*log2e
-      float cc = c_log2, bb = 0.f, tmax;
-      const bool full = (info & 4) != 0;
-      const bool pen_tile = PEN && wave_out && (info & 1);
-      if (full && (!pen_tile || (info & 2))) {
-        if (pen_tile) {
-          const float p = tara_pen(fabsf(qt - tuni_s[st]), a.window, a.inv_falloff, a.strength,
-                                   a.cap);
-          bb = q_out ? -p * kLog2e : 0.f;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[c][r]);
-        tmax = mx * cc + bb;
-      } else {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kl = kh * KW + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const uint32_t sg = kseg_s[st][kl];
-            float x = sacc[c][r] * cc;
-            if (sg == (uint32_t)kSegInvalid) {
-              x = -INFINITY;
-            } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
-              x -= tara_pen(fabsf(qt - kt_s[st][kl]), a.window, a.inv_falloff, a.strength,
-                            a.cap) * kLog2e;
-            }
-            sacc[c][r] = x;
-            mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) {
+          const int kl = kh * KW + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const uint32_t sg = ksg[kl];
+          float x = sacc[c][r] * cc;
+          if (sg == (uint32_t)kSegInvalid) {
+            x = -INFINITY;
+          } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
+            x -= tara_pen(fabsf(qt - ktt[kl]), a.window, a.inv_falloff, a.strength, a.cap) *
+                 kLog2e;
           }
+          sacc[c][r] = x;
+          mx = fmaxf(mx, x);
         }
-        cc = 1.f;
-        tmax = mx;
       }
-      tmax = pair_max(tmax);
-
-      // ---- online softmax with lazy rescale
-      if (__ballot(tmax > m_run + kLazyRescale) != 0ull) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      cc = 1.f;
+      tmax = mx;
+    }
+    tmax = pair_max(tmax);
+    if (__ballot(tmax > m_run + kLazyRescale) != 0ull) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mb = bb - (m_run == -INFINITY ? 0.f : m_run);
+    bf16x8 pb[NS];
+    float rs0 = 0.f, rs1 = 0.f;  // float32 row sums (two chains)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      f32x8 pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
+        if (e & 1) rs1 += pv[e]; else rs0 += pv[e];
       }
-      const float mb = bb - (m_run == -INFINITY ? 0.f : m_run);
-      bf16x8 pb[NS];
-      float rs = 0.f;
+      pb[s] = __builtin_convertvector(pv, bf16x8);
+    }
+    l_run += rs0 + rs1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dr = 32 * dt + l32;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
-          rs += p;
-          pv[e] = p;
-        }
-        pb[s] = __builtin_convertvector(pv, bf16x8);
-      }
-      l_run += rs;
-
-      // ---- O^T += V^T P^T
-      const uint16_t* vst = vs[st];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int dr = 32 * dt + l32;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int ch = kh * (KW / 8) + 2 * s + hh;
-          const bf16x8 va = *(const bf16x8*)&vst[dr * 64 + ((ch ^ (dr & 7)) * 8)];
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
-        }
+        const int ch = kh * (KW / 8) + 2 * s + hh;
+        const bf16x8 va = *(const bf16x8*)&vst[dr * 64 + ((ch ^ (dr & 7)) * 8)];
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
     }
-    if (more) lstore(st ^ 1);
+  };
+  auto compute = [&](int st, const uint16_t* kst, const uint16_t* vst, const uint8_t* ksg,
+                     const float* ktt) __attribute__((always_inline)) {
+    const int info = __builtin_amdgcn_readfirstlane(info_s[st]);
+    if (info & 8) return;
+    const bool full = (info & 4) != 0;
+    const bool pen_tile = PEN && wave_out && (info & 1);
+    if (full && (!pen_tile || (info & 2))) {
+      tile_body(std::false_type{}, kst, vst, ksg, ktt, pen_tile, tuni_s[st]);
+    } else {
+      tile_body(std::true_type{}, kst, vst, ksg, ktt, false, 0.f);
+    }
+  };
+
+  if (ntiles > 0) {
+    prefetch(0, ks0, vs0);
+    small_store(kseg0, kt0, 0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    // stage 0 holds tile it; fill stage 1 with tile it+1 meanwhile
+    const bool more1 = it + 1 < ntiles;
+    if (more1) prefetch(it + 1, ks1, vs1);
+    compute(0, ks0, vs0, kseg0, kt0);
+    if (more1) small_store(kseg1, kt1, 1);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = it + 2 < ntiles;
+    if (more2) prefetch(it + 2, ks0, vs0);
+    compute(1, ks1, vs1, kseg1, kt1);
+    if (more2) small_store(kseg0, kt0, 0);
     __syncthreads();
   }
 
   // ---- combine lane halves, then key halves (sparse), then normalise
   float l_tot = pair_sum(l_run);
-  if (KSPLIT == 2) {
-    float* ox = (float*)&ks[0][0];  // [ROWG][DT*16][64]
-    float* ml = (float*)&vs[0][0];  // [ROWG][2][64]
+  if constexpr (KSPLIT == 2) {
+    // partner partials: row group 0 in ks0, row group 1 in ks1 ([DT*16][64] floats each)
+    static_assert(ROWG == 2 && DT * 16 * 64 * 4 <= TILE_ELEMS * 2, "merge buffers fit");
+    float* ox = (float*)(rg == 0 ? &ks0[0] : &ks1[0]);
+    float* ml = (float*)&vs0[0];  // [ROWG][2][64]
     if (kh == 1) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ox[(rg * DT * 16 + dt * 16 + r) * 64 + lane] = oacc[dt][r];
+        for (int r = 0; r < 16; ++r) ox[(dt * 16 + r) * 64 + lane] = oacc[dt][r];
       ml[(rg * 2 + 0) * 64 + lane] = m_run;
       ml[(rg * 2 + 1) * 64 + lane] = l_tot;
     }
@@ -367,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          oacc[dt][r] = oacc[dt][r] * a0 + ox[(rg * DT * 16 + dt * 16 + r) * 64 + lane] * a1;
+          oacc[dt][r] = oacc[dt][r] * a0 + ox[(dt * 16 + r) * 64 + lane] * a1;
       l_tot = l_tot * a0 + l1 * a1;
       m_run = M;
     }

@@ -48,7 +48,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, 
 // Router.
 struct RouterWs {
   float* qbar;     // [H][nb][D]
-  float* kbar;     // [H][nb][D]
+  float* kbar;     // [H][D][nb] (d-major)
   int32_t* video;  // [nb]
   int32_t* counts; // [2]: n_prot, n_video
 };

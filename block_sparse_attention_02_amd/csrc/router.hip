@@ -126,16 +126,25 @@ __global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict
     }
   }
   const float cnt = (float)(hi - lo);
-  float* oq = qbar + ((int64_t)h * nb + b) * D + d0;
-  float* ok = kbar + ((int64_t)h * nb + b) * D + d0;
+  float* oq = qbar + ((int64_t)h * nb + b) * D + d0;   // [H][nb][D]
+  float* ok = kbar + ((int64_t)h * D + d0) * nb + b;   // [H][D][nb]
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     oq[i] = __fdiv_rn(aq[i], cnt);
-    ok[i] = __fdiv_rn(ak[i], cnt);
+    ok[(int64_t)i * nb] = __fdiv_rn(ak[i], cnt);
   }
 }
 
 // ------------------------------------------------------------------ 3. score + top-k
+// float32 product rounded on its own: the empty asm makes the value opaque, so the
+// following addition can never be contracted into a fused multiply-add (the file is
+// also compiled with -ffp-contract=off).
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+  float p = a * b;
+  __asm__("" : "+v"(p));
+  return p;
+}
+
 // Order-preserving map of a float32 score to an unsigned key: larger key = better;
 // -0 and +0 map together; NaN maps below every number.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -152,8 +161,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           const int32_t* __restrict__ counts,
                                                           int nb, int k_sel,
                                                           int32_t* __restrict__ tiles) {
-  extern __shared__ float sc[];  // [QB][nv]
-  __shared__ float qs[QB][D];
+  static_assert(QB == 1 || QB == 4, "query blocks per workgroup");
+  extern __shared__ float sc[];  // [QB][nv] pooled scores
+  __shared__ __attribute__((aligned(16))) float qs[D][QB];  // qbar, d-major
   __shared__ int hist[kTopkWaves][256];
   const int h = blockIdx.y;
   const int qb0 = blockIdx.x * QB;
@@ -164,20 +174,26 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
   for (int e = tid; e < QB * D; e += 256) {
     const int j = e / D, d = e % D;
-    qs[j][d] = (qb0 + j < nb) ? qbar[((int64_t)h * nb + qb0 + j) * D + d] : 0.f;
+    qs[d][j] = (qb0 + j < nb) ? qbar[((int64_t)h * nb + qb0 + j) * D + d] : 0.f;
   }
   __syncthreads();
+  // Lanes take consecutive video tiles, so each d reads one coalesced run of the
+  // d-major kbar; the QB query means of that d come from one LDS read.
+  const float* kh = kbar + (int64_t)h * D * nb;
   for (int vi = tid; vi < nv; vi += 256) {
-    const float* kr = kbar + ((int64_t)h * nb + video[vi]) * D;
+    const int kb = video[vi];
     float acc[QB];
 #pragma unroll
     for (int j = 0; j < QB; ++j) acc[j] = 0.f;
-    for (int d0 = 0; d0 < D; d0 += 4) {
-      const f32x4 kv = *(const f32x4*)(kr + d0);
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) {
+      const float kv = kh[(int64_t)d * nb + kb];
+      if (QB == 4) {
+        const f32x4 q4 = *(const f32x4*)&qs[d][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < QB; ++j) acc[j] = __fadd_rn(acc[j], __fmul_rn(qs[j][d0 + i], kv[i]));
+        for (int j = 0; j < 4; ++j) acc[j] = acc[j] + mul_rounded(q4[j], kv);
+      } else {
+        acc[0] = acc[0] + mul_rounded(qs[d][0], kv);
       }
     }
 #pragma unroll
