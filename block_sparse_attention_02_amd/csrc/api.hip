@@ -28,18 +28,23 @@ int check_tara(float strength, float window, float falloff, float cap, float sca
 bool dtype_ok(int dt) { return dt == H3_DTYPE_F32 || dt == H3_DTYPE_BF16; }
 bool dim_ok(int d) { return d == 64 || d == 128; }
 
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 size_t vt_bytes(int nk, int heads, int head_dim) {
   return (size_t)pad_keys(nk) * (size_t)heads * (size_t)head_dim * sizeof(uint16_t);
 }
 
-inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+// bf16 attention workspace: the transposed v copy, then the per-tile key summary.
+size_t attn_ws_bytes(int nk, int heads, int head_dim) {
+  return align256(vt_bytes(nk, heads, head_dim)) + align256((size_t)pad_keys(nk) / kTile * sizeof(TileInfo));
+}
 
 AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, int heads,
                    const uint8_t* q_seg, const float* q_t, const uint8_t* k_seg,
                    const float* k_t, float strength, float window, float falloff, float cap,
                    float scale, void* o, int o_dtype, float* lse) {
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.vt = nullptr;
+  a.q = q; a.k = k; a.v = v; a.vt = nullptr; a.tinfo = nullptr;
   a.q_seg = q_seg; a.q_t = q_t; a.k_seg = k_seg; a.k_t = k_t;
   a.o = o; a.lse = lse;
   a.nq = nq; a.nk = nk; a.nkp = (int)pad_keys(nk); a.H = heads;
@@ -50,16 +55,27 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, 
   return a;
 }
 
-// One attention launch over (queries, keys); the bf16 path first writes the
-// transposed v copy into `vt` unless `vt_ready` says it is already there.
+// Fills a bf16 attention workspace for the keys of `a`: the transposed v copy and the
+// per-tile key summary.
+hipError_t prepare_keys(const AttnArgs& a, int head_dim, void* ws, hipStream_t s) {
+  char* w = (char*)ws;
+  hipError_t e = launch_vt_transpose((const uint16_t*)a.v, (uint16_t*)w, a.nk, a.H, head_dim, s);
+  if (e != hipSuccess) return e;
+  return launch_tile_info(a.k_seg, a.k_t, a.nk,
+                          (TileInfo*)(w + align256(vt_bytes(a.nk, a.H, head_dim))), s);
+}
+
+// One attention launch over (queries, keys); the bf16 path first prepares the key
+// workspace unless `ready` says it already holds these keys.
 hipError_t run_attention(AttnArgs a, int dtype, int head_dim, bool sparse, bool penalty,
-                         uint16_t* vt, bool vt_ready, hipStream_t s) {
+                         void* ws, bool ready, hipStream_t s) {
   if (dtype == H3_DTYPE_BF16) {
-    if (!vt_ready) {
-      hipError_t e = launch_vt_transpose((const uint16_t*)a.v, vt, a.nk, a.H, head_dim, s);
+    if (!ready) {
+      hipError_t e = prepare_keys(a, head_dim, ws, s);
       if (e != hipSuccess) return e;
     }
-    a.vt = vt;
+    a.vt = (const uint16_t*)ws;
+    a.tinfo = (const TileInfo*)((const char*)ws + align256(vt_bytes(a.nk, a.H, head_dim)));
     return launch_attn_bf16(a, head_dim, sparse, penalty, s);
   }
   return launch_attn_f32(a, head_dim, sparse, penalty, s);
@@ -131,7 +147,7 @@ ViaPlan make_plan(const uint8_t* seg, const float* t, int n, int heads, int head
   if (dtype == H3_DTYPE_BF16) {
     for (const Run& r : p.vt_ranges) {
       p.vt_off.push_back(off);
-      off += align256(vt_bytes(r.b - r.a, heads, head_dim));
+      off += attn_ws_bytes(r.b - r.a, heads, head_dim);
     }
   }
   for (const Run& r : p.out_q) p.max_out_rows = std::max(p.max_out_rows, r.b - r.a);
@@ -178,7 +194,7 @@ const char* h3attn_status_string(int status) {
 
 size_t attn_dense_tara_workspace(int nk, int heads, int head_dim, int dtype) {
   if (nk <= 0 || heads <= 0 || !dim_ok(head_dim) || dtype != H3_DTYPE_BF16) return 0;
-  return vt_bytes(nk, heads, head_dim);
+  return attn_ws_bytes(nk, heads, head_dim);
 }
 
 int attn_dense_tara(const void* q, const void* k, const void* v, int dtype, int nq, int nk,
@@ -196,8 +212,7 @@ int attn_dense_tara(const void* q, const void* k, const void* v, int dtype, int 
   AttnArgs a = make_args(q, k, v, nq, nk, heads, q_seg, q_t, k_seg, k_t, strength, window,
                          falloff, cap, scale, o, o_dtype, lse);
   const bool pen = strength > 0.f && cap > 0.f;
-  hipError_t e = run_attention(a, dtype, head_dim, false, pen, (uint16_t*)ws, false,
-                               (hipStream_t)stream);
+  hipError_t e = run_attention(a, dtype, head_dim, false, pen, ws, false, (hipStream_t)stream);
   return e == hipSuccess ? H3_OK : H3_ELAUNCH;
 }
 
@@ -288,8 +303,7 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, in
   a.k_sel = k_sel;
   a.nqb = (n + kTile - 1) / kTile;
   const bool pen = strength > 0.f && cap > 0.f;
-  hipError_t e = run_attention(a, dtype, head_dim, true, pen, (uint16_t*)ws, false,
-                               (hipStream_t)stream);
+  hipError_t e = run_attention(a, dtype, head_dim, true, pen, ws, false, (hipStream_t)stream);
   return e == hipSuccess ? H3_OK : H3_ELAUNCH;
 }
 
@@ -338,13 +352,14 @@ int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, 
   float* part = (float*)(w + p.part_off);
   float* part_lse = (float*)(w + p.part_lse_off);
 
-  // Transposed v copies, one per key range used below.
+  // Key workspaces (transposed v copy + tile summary), one per key range used below.
   if (dtype == H3_DTYPE_BF16) {
     for (size_t i = 0; i < p.vt_ranges.size(); ++i) {
       const Run& r = p.vt_ranges[i];
-      if (launch_vt_transpose((const uint16_t*)vrow(r.a), (uint16_t*)(w + p.vt_off[i]),
-                              r.b - r.a, heads, D, s) != hipSuccess)
-        return H3_ELAUNCH;
+      AttnArgs ka = make_args(qrow(r.a), krow(r.a), vrow(r.a), r.b - r.a, r.b - r.a, heads,
+                              seg + r.a, t + r.a, seg + r.a, t + r.a, 0.f, window, falloff,
+                              cap, scale, nullptr, H3_DTYPE_F32, nullptr);
+      if (prepare_keys(ka, D, w + p.vt_off[i], s) != hipSuccess) return H3_ELAUNCH;
     }
   }
   // Ordinary attention of query rows [qa, qb) over key rows [ka, kb) into (out, out_lse).
@@ -353,9 +368,13 @@ int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, 
     AttnArgs a = make_args(qrow(qa), krow(ka), vrow(ka), qb - qa, kb - ka, heads, seg + qa,
                            t + qa, seg + ka, t + ka, 0.f, window, falloff, cap, scale, out,
                            out_dtype, out_lse);
-    uint16_t* vt = nullptr;
-    if (dtype == H3_DTYPE_BF16) vt = (uint16_t*)(w + p.vt_off[vt_slot(p, ka, kb)]);
-    return run_attention(a, dtype, D, false, false, vt, true, s) == hipSuccess;
+    void* kws = nullptr;
+    if (dtype == H3_DTYPE_BF16) {
+      const int slot = vt_slot(p, ka, kb);
+      if (slot < 0) return false;
+      kws = w + p.vt_off[slot];
+    }
+    return run_attention(a, dtype, D, false, false, kws, true, s) == hipSuccess;
   };
 
   // Queries outside the output video: one ordinary call over every key.

@@ -106,7 +106,46 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t* __res
   }
 }
 
+// ------------------------------------------------------------------ tile info
+// Per 64-key tile: bit0 any guide key, bit1 every key a guide row of one frame,
+// bit2 all 64 keys present; .t = time of the tile's first key.
+__global__ __launch_bounds__(64) void tile_info_kernel(const uint8_t* __restrict__ k_seg,
+                                                       const float* __restrict__ k_t, int nk,
+                                                       TileInfo* __restrict__ info) {
+  const int kb = blockIdx.x;
+  const int key = kb * 64 + threadIdx.x;
+  const bool valid = key < nk;
+  const uint32_t sg = valid ? (uint32_t)k_seg[key] : (uint32_t)kSegInvalid;
+  const float tt = valid ? k_t[key] : 0.f;
+  const uint64_t g = __ballot(sg == (uint32_t)kSegGuide);
+  const uint64_t full = __ballot(valid);
+  const float t0 = __shfl(tt, 0);
+  const uint64_t same = __ballot(tt == t0);
+  if (threadIdx.x == 0) {
+    int f = 0;
+    if (g) f |= kTileAnyGuide;
+    if (g == ~0ull && same == ~0ull) f |= kTileUniformGuide;
+    if (full == ~0ull) f |= kTileFull;
+    info[kb] = TileInfo{f, t0};
+  }
+}
+
 // ------------------------------------------------------------------ attention
+// LDS layouts (bf16, 16-byte chunks, XOR-swizzled so that every 8- and 16-lane phase
+// of a 128-bit operand read touches distinct banks):
+//   K   : row = key (D*2 bytes); chunk c of key r sits at chunk c ^ (r & 15) (D = 128)
+//         or c ^ (r & 7) (D = 64).
+//   V^T : rows d and d+1 share a 256-byte line p = d/2; chunk c of row d sits at
+//         (8*(d&1) + c) ^ ((p & 15) ^ 4*(d&1)).
+template <int D>
+__device__ __forceinline__ int k_lds_chunk(int r, int c) {
+  return D == 128 ? (c ^ (r & 15)) : (c ^ (r & 7));
+}
+__device__ __forceinline__ int vt_lds_byte(int d, int c) {
+  const int p = d >> 1, b = d & 1;
+  return p * 256 + (((8 * b + c) ^ ((p & 15) ^ (4 * b))) * 16);
+}
+
 template <int D, int ROWG, int KSPLIT, bool SPARSE, bool PEN>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   static_assert(ROWG * KSPLIT == 4, "four waves per workgroup");
@@ -128,9 +167,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t vs1[TILE_ELEMS];
   __shared__ uint8_t kseg0[64], kseg1[64];
   __shared__ float kt0[64], kt1[64];
-  __shared__ int info_s[2];     // bit0 any guide key, bit1 all keys guide of one frame,
-                                // bit2 all 64 keys valid, bit3 tile skipped
-  __shared__ float tuni_s[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
   const uint16_t* __restrict__ kp = (const uint16_t*)a.k;
   const uint16_t* __restrict__ vtp = a.vt;
+  const TileInfo* __restrict__ tinfo = a.tinfo;
   const float c_log2 = a.scale * kLog2e;
 
   const int qrow = qblk * BM + rg * 32 + l32;
@@ -161,7 +198,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   }
   const float qt = qvalid ? a.q_t[qrow] : 0.f;
   const bool q_out = PEN && qvalid && a.q_seg[qrow] == kSegOutput;
-  const bool wave_out = PEN && (__ballot(q_out) != 0ull);
+  // does any query row of this workgroup take the penalty?
+  const bool pen_wg = PEN && __syncthreads_or(q_out);
 
   const int nkb = (a.nk + 63) / 64;
   int ntiles;
@@ -172,24 +210,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   } else {
     ntiles = nkb;
   }
-  auto tile_of = [&](int i) -> int __attribute__((always_inline)) {
-    int kb = i;
-    if (SPARSE) kb = i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
-    return __builtin_amdgcn_readfirstlane(kb);
-  };
 
-  // ---- tile loads: K and V^T straight into LDS with buffer loads (one 16-byte chunk per
-  // lane per instruction, 1 KB per wave instruction). Each lane's byte offset inside a
-  // tile is fixed, so it is computed once; the tile base lives in a scalar descriptor.
-  // K rows past the end of the sequence fall outside the descriptor and are masked.
+  // ---- per-lane byte offsets of this thread's DMA chunks inside a tile (fixed)
   uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int off = (wave * DMA_PER_WAVE + i) * 1024 + lane * 16;  // byte offset in tile
-    const int r = off / KROW_BYTES, pc = (off % KROW_BYTES) / 16;    // key row, chunk
-    koff[i] = (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)((pc ^ (r & 7)) * 16);
-    const int d = off / 128, vc = (off % 128) / 16;                  // V^T row, chunk
-    voff[i] = (uint32_t)d * (uint32_t)(a.nkp * 2) + (uint32_t)((vc ^ (d & 7)) * 16);
+    const int off = (wave * DMA_PER_WAVE + i) * 1024 + lane * 16;  // LDS byte offset
+    const int r = off / KROW_BYTES, pc = (off % KROW_BYTES) / 16;    // key row, chunk slot
+    koff[i] = (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)(k_lds_chunk<D>(r, pc) * 16);
+    // invert the V^T layout: slot -> (row d, logical chunk c)
+    const int p = off / 256, slot = (off % 256) / 16;
+    const int b = ((slot ^ (p & 15)) >> 3) & 1;
+    const int c = (slot ^ ((p & 15) ^ (4 * b))) & 7;
+    voff[i] = (uint32_t)(2 * p + b) * (uint32_t)(a.nkp * 2) + (uint32_t)(c * 16);
   }
   auto dma = [&](int kb, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
     const int k0 = kb * 64;
@@ -205,39 +238,56 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < DMA_PER_WAVE; ++i)
       buffer_to_lds16(vbase, vbytes, vdst + (wave * DMA_PER_WAVE + i) * 512, voff[i]);
   };
+  // row segment ids and times of a tile (per-key tiles only)
   uint32_t sreg = kSegInvalid;
   float treg = 0.f;
   auto small_load = [&](int kb) __attribute__((always_inline)) {
     if (tid < 64) {
       const int key = kb * 64 + tid;
-      const bool kv = kb >= 0 && kb < nkb && key < a.nk;
+      const bool kv = key < a.nk;
       sreg = kv ? (uint32_t)a.k_seg[key] : (uint32_t)kSegInvalid;
       treg = kv ? a.k_t[key] : 0.f;
     }
   };
-  auto small_store = [&](uint8_t* sg, float* tt, int st) __attribute__((always_inline)) {
+  auto small_store = [&](uint8_t* sg, float* tt) __attribute__((always_inline)) {
     if (tid < 64) {
       sg[tid] = (uint8_t)sreg;
       tt[tid] = treg;
-      const uint64_t g = __ballot(sreg == (uint32_t)kSegGuide);
-      const uint64_t valid = __ballot(sreg != (uint32_t)kSegInvalid);
-      const float t0 = __shfl(treg, 0);
-      const uint64_t same = __ballot(treg == t0);
-      if (tid == 0) {
-        int info = 0;
-        if (g) info |= 1;
-        if (g == ~0ull && same == ~0ull) info |= 2;
-        if (valid == ~0ull) info |= 4;
-        if (valid == 0ull) info |= 8;
-        info_s[st] = info;
-        tuni_s[st] = t0;
-      }
     }
   };
-  auto prefetch = [&](int i, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
-    const int kb = tile_of(i);
-    if (kb >= 0 && kb < nkb) dma(kb, kdst, vdst);
-    small_load(kb);
+
+  // ---- tile classes: a tile is "fast" for this workgroup when all 64 keys are
+  // present and its penalty is one scalar per query (no guide key, no query that takes
+  // the penalty, or every key a guide row of one frame); every other tile is per-key.
+  auto is_fast = [&](int flags) __attribute__((always_inline)) -> bool {
+    return (flags & kTileFull) &&
+           (!pen_wg || !(flags & kTileAnyGuide) || (flags & kTileUniformGuide));
+  };
+  // Walks the tile list in order, yielding the entries of one class. Each wave reads
+  // 64 entries at a time and keeps a ballot mask of the matching ones.
+  struct Cursor { int chunk; uint64_t mask; int kb_lane; int flags_lane; float t_lane; };
+  struct Tile { int kb; int flags; float t; };
+  auto cursor_next = [&](Cursor& cu, bool want_fast, Tile& tl) __attribute__((always_inline)) -> int {
+    while (cu.mask == 0ull) {
+      ++cu.chunk;
+      if (cu.chunk * 64 >= ntiles) return ntiles;
+      const int i = cu.chunk * 64 + lane;
+      int kb = -1;
+      if (i < ntiles) kb = SPARSE ? (i < a.n_prot ? a.prot[i] : rt[i - a.n_prot]) : i;
+      const bool ok = kb >= 0 && kb < nkb;
+      TileInfo ti{0, 0.f};
+      if (ok) ti = tinfo[kb];
+      cu.mask = __ballot(ok && (is_fast(ti.flags) == want_fast));
+      cu.kb_lane = kb;
+      cu.flags_lane = ti.flags;
+      cu.t_lane = ti.t;
+    }
+    const int bit = __builtin_ctzll(cu.mask);
+    cu.mask &= cu.mask - 1;
+    tl.kb = __builtin_amdgcn_readfirstlane(__shfl(cu.kb_lane, bit));
+    tl.flags = __builtin_amdgcn_readfirstlane(__shfl(cu.flags_lane, bit));
+    tl.t = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__shfl(cu.t_lane, bit))));
+    return cu.chunk * 64 + bit;
   };
 
   f32x16 oacc[DT];
@@ -249,11 +299,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;
 
   // ---- one tile: S^T = K Q^T, scores with the penalty, online softmax, O^T += V^T P^T.
-  // GENERAL handles masked keys and per-key penalties; the fast body covers tiles
-  // whose penalty is one scalar per query (or zero).
   auto tile_body = [&](auto general_tag, const uint16_t* kst, const uint16_t* vst,
-                       const uint8_t* ksg, const float* ktt, bool uniform_guide,
-                       float tuni) __attribute__((always_inline)) {
+                       const uint8_t* ksg, const float* ktt, const Tile& tl) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
     f32x16 sacc[NT];
 #pragma unroll
@@ -265,21 +312,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         const int kr = kh * KW + 32 * c + l32;
-        const bf16x8 ka = *(const bf16x8*)&kst[kr * D + (((2 * s + hh) ^ (kr & 7)) * 8)];
+        const bf16x8 ka = *(const bf16x8*)&kst[kr * D + k_lds_chunk<D>(kr, 2 * s + hh) * 8];
         sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
       }
     }
     float cc = c_log2, bb = 0.f, tmax;
-    if (!GENERAL) {
-      if (PEN && uniform_guide && q_out) {
-        // every key is a guide row of one frame: one penalty per output query row
-        bb = -tara_pen(fabsf(qt - tuni), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
-      }
+    if constexpr (!GENERAL) {
+      if (PEN && pen_wg && (tl.flags & kTileUniformGuide) && q_out)
+        bb = -tara_pen(fabsf(qt - tl.t), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
       float mx = -INFINITY;
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[c][r], sacc[c][r + 1]));
+        for (int r = 0; r < 16; r += 2)
+          mx = __builtin_elementwise_maximum(
+              __builtin_elementwise_maximum(mx, sacc[c][r]), sacc[c][r + 1]);
       tmax = mx * cc + bb;
     } else {
       float mx = -INFINITY;
@@ -297,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                  kLog2e;
           }
           sacc[c][r] = x;
-          mx = fmaxf(mx, x);
+          mx = __builtin_elementwise_maximum(mx, x);
         }
       }
       cc = 1.f;
@@ -305,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     tmax = pair_max(tmax);
     if (__ballot(tmax > m_run + kLazyRescale) != 0ull) {
-      const float m_new = fmaxf(m_run, tmax);
+      const float m_new = __builtin_elementwise_maximum(m_run, tmax);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -328,49 +375,55 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       pb[s] = __builtin_convertvector(pv, bf16x8);
     }
     l_run += rs0 + rs1;
+    const char* vsb = (const char*)vst;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int dr = 32 * dt + l32;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int ch = kh * (KW / 8) + 2 * s + hh;
-        const bf16x8 va = *(const bf16x8*)&vst[dr * 64 + ((ch ^ (dr & 7)) * 8)];
+        const bf16x8 va = *(const bf16x8*)(vsb + vt_lds_byte(dr, ch));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
     }
   };
-  auto compute = [&](int st, const uint16_t* kst, const uint16_t* vst, const uint8_t* ksg,
-                     const float* ktt) __attribute__((always_inline)) {
-    const int info = __builtin_amdgcn_readfirstlane(info_s[st]);
-    if (info & 8) return;
-    const bool full = (info & 4) != 0;
-    const bool pen_tile = PEN && wave_out && (info & 1);
-    if (full && (!pen_tile || (info & 2))) {
-      tile_body(std::false_type{}, kst, vst, ksg, ktt, pen_tile, tuni_s[st]);
-    } else {
-      tile_body(std::true_type{}, kst, vst, ksg, ktt, false, 0.f);
+
+  // ---- one pass over the tiles of one class, double-buffered: while stage s is
+  // consumed, the next tile of the class streams into the other stage.
+  auto run_pass = [&](auto general_tag) __attribute__((always_inline)) {
+    constexpr bool GENERAL = decltype(general_tag)::value;
+    Cursor cu{-1, 0ull, -1, 0, 0.f};
+    Tile t_cur{-1, 0, 0.f}, t_nxt{-1, 0, 0.f}, t_nn{-1, 0, 0.f};
+    int cur = cursor_next(cu, !GENERAL, t_cur);
+    if (cur < ntiles) {
+      dma(t_cur.kb, ks0, vs0);
+      if (GENERAL) { small_load(t_cur.kb); small_store(kseg0, kt0); }
+    }
+    __syncthreads();
+    while (cur < ntiles) {
+      const int nxt = cursor_next(cu, !GENERAL, t_nxt);
+      if (nxt < ntiles) {
+        dma(t_nxt.kb, ks1, vs1);
+        if (GENERAL) small_load(t_nxt.kb);
+      }
+      tile_body(general_tag, ks0, vs0, kseg0, kt0, t_cur);
+      if (GENERAL && nxt < ntiles) small_store(kseg1, kt1);
+      __syncthreads();
+      if (nxt >= ntiles) break;
+      const int nn = cursor_next(cu, !GENERAL, t_nn);
+      if (nn < ntiles) {
+        dma(t_nn.kb, ks0, vs0);
+        if (GENERAL) small_load(t_nn.kb);
+      }
+      tile_body(general_tag, ks1, vs1, kseg1, kt1, t_nxt);
+      if (GENERAL && nn < ntiles) small_store(kseg0, kt0);
+      __syncthreads();
+      cur = nn;
+      t_cur = t_nn;
     }
   };
-
-  if (ntiles > 0) {
-    prefetch(0, ks0, vs0);
-    small_store(kseg0, kt0, 0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    // stage 0 holds tile it; fill stage 1 with tile it+1 meanwhile
-    const bool more1 = it + 1 < ntiles;
-    if (more1) prefetch(it + 1, ks1, vs1);
-    compute(0, ks0, vs0, kseg0, kt0);
-    if (more1) small_store(kseg1, kt1, 1);
-    __syncthreads();
-    if (!more1) break;
-    const bool more2 = it + 2 < ntiles;
-    if (more2) prefetch(it + 2, ks0, vs0);
-    compute(1, ks1, vs1, kseg1, kt1);
-    if (more2) small_store(kseg0, kt0, 0);
-    __syncthreads();
-  }
+  run_pass(std::false_type{});
+  run_pass(std::true_type{});
 
   // ---- combine lane halves, then key halves (sparse), then normalise
   float l_tot = pair_sum(l_run);
@@ -391,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     if (kh == 0) {
       const float m1 = ml[(rg * 2 + 0) * 64 + lane];
       const float l1 = ml[(rg * 2 + 1) * 64 + lane];
-      const float M = fmaxf(m_run, m1);
+      const float M = __builtin_elementwise_maximum(m_run, m1);
       const float a0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
       const float a1 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
 #pragma unroll
@@ -448,6 +501,12 @@ hipError_t launch_vt_transpose(const uint16_t* v, uint16_t* vt, int nk, int H, i
     vt_transpose_kernel<128><<<grid, 256, 0, s>>>(v, vt, nk, nkp, H);
   else
     vt_transpose_kernel<64><<<grid, 256, 0, s>>>(v, vt, nk, nkp, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_info(const uint8_t* k_seg, const float* k_t, int nk, TileInfo* info,
+                            hipStream_t s) {
+  tile_info_kernel<<<(nk + 63) / 64, 64, 0, s>>>(k_seg, k_t, nk, info);
   return hipGetLastError();
 }
 

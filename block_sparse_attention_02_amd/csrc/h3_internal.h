@@ -11,12 +11,20 @@ constexpr int kTile = 64;         // key tile = routing block = 64 rows
 constexpr int kSegText = 0, kSegGuide = 1, kSegAudio = 2, kSegOutput = 3;
 constexpr int kSegInvalid = 255;  // marks key slots past the end of a tile
 
+// Per 64-key tile summary (see tile_info_kernel).
+constexpr int kTileAnyGuide = 1, kTileUniformGuide = 2, kTileFull = 4;
+struct TileInfo {
+  int flags;
+  float t;
+};
+
 // Arguments of one attention launch (dense or block-sparse).
 struct AttnArgs {
   const void* q;            // [nq][H][D]  (bf16 bits or f32)
   const void* k;            // [nk][H][D]
   const void* v;            // [nk][H][D]  (f32 path)
   const uint16_t* vt;       // [H][D][nkp] bf16, keys permuted in 16-groups (bf16 path)
+  const TileInfo* tinfo;    // [ceil(nk/64)] (bf16 path)
   const uint8_t* q_seg;
   const float* q_t;
   const uint8_t* k_seg;
@@ -41,6 +49,8 @@ inline int64_t pad_keys(int64_t nk) { return (nk + kTile - 1) / kTile * kTile; }
 // bf16 path: transposes v into vt (see attn_bf16.hip), then runs attention.
 hipError_t launch_vt_transpose(const uint16_t* v, uint16_t* vt, int nk, int H, int D,
                                hipStream_t s);
+hipError_t launch_tile_info(const uint8_t* k_seg, const float* k_t, int nk, TileInfo* info,
+                            hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
 // float32 path.
 hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
