@@ -8,9 +8,10 @@
 // frame share the same temporal correction, section 3); mixed and ragged tiles take a
 // per-element path. No rows x rows bias is ever formed.
 //
-// Work decomposition (one workgroup = 4 waves of 64 lanes):
-//   dense : 128 query rows, wave w owns rows 32w..32w+31 and all 64 keys of each tile;
-//   sparse: one 64-row query block, wave w owns rows 32(w%2).. and keys 32(w/2).. of
+// Work decomposition (waves of 64 lanes, two per SIMD):
+//   dense : 8 waves, 256 query rows, wave w owns rows 32w..32w+31 and all 64 keys of
+//           each tile, so each K/V tile load serves 256 queries;
+//   sparse: 4 waves, one 64-row query block, wave w owns rows 32(w%2).. and keys 32(w/2).. of
 //           each routed tile; the two key halves are merged at the end.
 // Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
 // lane holds one query column; softmax row reductions stay in registers plus one
@@ -147,8 +148,9 @@ __device__ __forceinline__ int vt_lds_byte(int d, int c) {
 }
 
 template <int D, int ROWG, int KSPLIT, bool SPARSE, bool PEN>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-  static_assert(ROWG * KSPLIT == 4, "four waves per workgroup");
+__global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int NW = ROWG * KSPLIT;   // waves per workgroup (4 or 8; two waves per SIMD)
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   constexpr int BM = 32 * ROWG;       // query rows per workgroup
   constexpr int KW = 64 / KSPLIT;     // keys of a tile handled by one wave
   constexpr int NT = KW / 32;         // 32x32 score tiles per wave
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int DK = D / 16;          // k-steps of the QK product
   constexpr int DT = D / 32;          // 32-row output tiles (over d)
   constexpr int TILE_ELEMS = 64 * D;  // bf16 elements of one K (or V^T) tile
-  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / 4;  // 1 KB wave loads per wave
+  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / NW;  // 1 KB wave loads per wave
   constexpr int KROW_BYTES = D * 2;
 
   // Two stages, each its own LDS object so the compiler can tell the stage being
@@ -485,8 +487,8 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t s) {
     dim3 grid(a.nqb, a.H);
     attn_bf16_kernel<D, 2, 2, true, PEN><<<grid, 256, 0, s>>>(a);
   } else {
-    dim3 grid((a.nq + 127) / 128, a.H);
-    attn_bf16_kernel<D, 4, 1, false, PEN><<<grid, 256, 0, s>>>(a);
+    dim3 grid((a.nq + 255) / 256, a.H);
+    attn_bf16_kernel<D, 8, 1, false, PEN><<<grid, 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }
