@@ -293,6 +293,7 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, in
   if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || block_size != kTile ||
       heads > 65535)
     return H3_EUNSUPPORTED;
+  if ((n + kTile - 1) / kTile > kMaxBlocks) return H3_EUNSUPPORTED;
   const size_t need = attn_block_sparse_workspace(n, heads, head_dim, dtype);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
   AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,

@@ -8,11 +8,16 @@
 // frame share the same temporal correction, section 3); mixed and ragged tiles take a
 // per-element path. No rows x rows bias is ever formed.
 //
-// Work decomposition (waves of 64 lanes, two per SIMD):
-//   dense : 8 waves, 256 query rows, wave w owns rows 32w..32w+31 and all 64 keys of
-//           each tile, so each K/V tile load serves 256 queries;
-//   sparse: 4 waves, one 64-row query block, wave w owns rows 32(w%2).. and keys 32(w/2).. of
-//           each routed tile; the two key halves are merged at the end.
+// Work decomposition: 8 waves of 64 lanes (two per SIMD), 256 query rows per
+// workgroup; wave w owns rows 32w..32w+31 and all 64 keys of each tile, so each K/V
+// tile load serves up to 256 queries.
+//   dense : every key tile, in order;
+//   sparse: the workgroup's rows are four 64-row query blocks. Their attended tiles
+//           (the protected tiles plus each block's routed tiles) are collected as bitmaps
+//           in LDS, and the workgroup walks the union in ascending tile order: every tile
+//           is loaded once for all four blocks and each wave computes only the tiles its
+//           own block attends. Routed lists of neighbouring blocks overlap heavily when
+//           the blocks share a video frame, so most loads serve the whole workgroup.
 // Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
 // lane holds one query column; softmax row reductions stay in registers plus one
 // exchange between lane halves.
@@ -147,12 +152,12 @@ __device__ __forceinline__ int vt_lds_byte(int d, int c) {
   return p * 256 + (((8 * b + c) ^ ((p & 15) ^ (4 * b))) * 16);
 }
 
-template <int D, int ROWG, int KSPLIT, bool SPARSE, bool PEN>
-__global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NW = ROWG * KSPLIT;   // waves per workgroup (4 or 8; two waves per SIMD)
-  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
-  constexpr int BM = 32 * ROWG;       // query rows per workgroup
-  constexpr int KW = 64 / KSPLIT;     // keys of a tile handled by one wave
+template <int D, bool SPARSE, bool PEN>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int NW = 8;               // waves per workgroup (two per SIMD)
+  constexpr int BM = 32 * NW;         // query rows per workgroup
+  constexpr int QB = BM / kTile;      // query blocks per workgroup (sparse)
+  constexpr int KW = 64;              // keys of a tile handled by one wave
   constexpr int NT = KW / 32;         // 32x32 score tiles per wave
   constexpr int NS = KW / 16;         // k-steps of the PV product
   constexpr int DK = D / 16;          // k-steps of the QK product
@@ -169,12 +174,13 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   __shared__ __attribute__((aligned(1024))) uint16_t vs1[TILE_ELEMS];
   __shared__ uint8_t kseg0[64], kseg1[64];
   __shared__ float kt0[64], kt1[64];
+  // sparse: bitmap 0 = protected tiles, bitmap 1 + j = routed tiles of query block j
+  __shared__ uint32_t tile_bits[SPARSE ? (QB + 1) * kBitmapWords : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rg = wave % ROWG;
-  const int kh = wave / ROWG;
+  const int rg = wave;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int qblk = blockIdx.x;
@@ -204,13 +210,35 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   const bool pen_wg = PEN && __syncthreads_or(q_out);
 
   const int nkb = (a.nk + 63) / 64;
-  int ntiles;
-  const int32_t* rt = nullptr;
-  if (SPARSE) {
-    ntiles = a.n_prot + a.k_sel;
-    rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
-  } else {
-    ntiles = nkb;
+  const int ntiles = nkb;  // tiles are visited in ascending order; the cursor skips
+                           // the ones no wave of this workgroup attends
+  // query blocks of this workgroup that exist (bit j = block QB*qblk + j)
+  int qb_valid = 0;
+  // this wave's bit in a tile's attend mask
+  const int my_qbit = 1 << (rg * 32 / kTile);
+  if constexpr (SPARSE) {
+    const int words = (nkb + 31) >> 5;  // the cursor reads no word past these
+    for (int i = tid; i < (QB + 1) * words; i += 64 * NW)
+      tile_bits[(i / words) * kBitmapWords + i % words] = 0u;
+    __syncthreads();
+    for (int i = tid; i < a.n_prot; i += 64 * NW) {
+      const int kb = a.prot[i];
+      if (kb >= 0 && kb < nkb) atomicOr(&tile_bits[kb >> 5], 1u << (kb & 31));
+    }
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int qb = qblk * QB + j;
+      if (qb < a.nqb) {
+        qb_valid |= 1 << j;
+        const int32_t* lst = a.tiles + ((int64_t)h * a.nqb + qb) * a.k_sel;
+        for (int i = tid; i < a.k_sel; i += 64 * NW) {
+          const int kb = lst[i];
+          if (kb >= 0 && kb < nkb)
+            atomicOr(&tile_bits[(1 + j) * kBitmapWords + (kb >> 5)], 1u << (kb & 31));
+        }
+      }
+    }
+    __syncthreads();
   }
 
   // ---- per-lane byte offsets of this thread's DMA chunks inside a tile (fixed)
@@ -267,29 +295,46 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   };
   // Walks the tile list in order, yielding the entries of one class. Each wave reads
   // 64 entries at a time and keeps a ballot mask of the matching ones.
-  struct Cursor { int chunk; uint64_t mask; int kb_lane; int flags_lane; float t_lane; };
-  struct Tile { int kb; int flags; float t; };
+  // Walks the key tiles in ascending order, yielding those of one class that some
+  // wave attends. Each wave examines 64 tiles at a time and keeps a ballot mask of
+  // the matching ones; .qmask says which query blocks attend the tile (sparse).
+  struct Cursor { int chunk; uint64_t mask; int flags_lane; float t_lane; int qm_lane; };
+  struct Tile { int kb; int flags; float t; int qmask; };
   auto cursor_next = [&](Cursor& cu, bool want_fast, Tile& tl) __attribute__((always_inline)) -> int {
     while (cu.mask == 0ull) {
       ++cu.chunk;
       if (cu.chunk * 64 >= ntiles) return ntiles;
-      const int i = cu.chunk * 64 + lane;
-      int kb = -1;
-      if (i < ntiles) kb = SPARSE ? (i < a.n_prot ? a.prot[i] : rt[i - a.n_prot]) : i;
-      const bool ok = kb >= 0 && kb < nkb;
+      const int kb = cu.chunk * 64 + lane;
+      int qm = 0;
       TileInfo ti{0, 0.f};
-      if (ok) ti = tinfo[kb];
-      cu.mask = __ballot(ok && (is_fast(ti.flags) == want_fast));
-      cu.kb_lane = kb;
+      if (kb < nkb) {
+        if constexpr (SPARSE) {
+          const int w = kb >> 5;
+          const uint32_t b = 1u << (kb & 31);
+          if (tile_bits[w] & b) {
+            qm = qb_valid;
+          } else {
+#pragma unroll
+            for (int j = 0; j < QB; ++j)
+              if (tile_bits[(1 + j) * kBitmapWords + w] & b) qm |= 1 << j;
+          }
+        } else {
+          qm = 1;
+        }
+        if (qm) ti = tinfo[kb];
+      }
+      cu.mask = __ballot(qm != 0 && (is_fast(ti.flags) == want_fast));
       cu.flags_lane = ti.flags;
       cu.t_lane = ti.t;
+      cu.qm_lane = qm;
     }
     const int bit = __builtin_ctzll(cu.mask);
     cu.mask &= cu.mask - 1;
-    tl.kb = __builtin_amdgcn_readfirstlane(__shfl(cu.kb_lane, bit));
+    tl.kb = cu.chunk * 64 + bit;
     tl.flags = __builtin_amdgcn_readfirstlane(__shfl(cu.flags_lane, bit));
     tl.t = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__shfl(cu.t_lane, bit))));
-    return cu.chunk * 64 + bit;
+    tl.qmask = SPARSE ? __builtin_amdgcn_readfirstlane(__shfl(cu.qm_lane, bit)) : 1;
+    return tl.kb;
   };
 
   f32x16 oacc[DT];
@@ -304,6 +349,7 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   auto tile_body = [&](auto general_tag, const uint16_t* kst, const uint16_t* vst,
                        const uint8_t* ksg, const float* ktt, const Tile& tl) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
+    if (SPARSE && !(tl.qmask & my_qbit)) return;  // this wave's block skips the tile
     f32x16 sacc[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c)
@@ -313,7 +359,7 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
     for (int s = 0; s < DK; ++s) {
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
-        const int kr = kh * KW + 32 * c + l32;
+        const int kr = 32 * c + l32;
         const bf16x8 ka = *(const bf16x8*)&kst[kr * D + k_lds_chunk<D>(kr, 2 * s + hh) * 8];
         sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
       }
@@ -336,7 +382,7 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
       for (int c = 0; c < NT; ++c) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kl = kh * KW + 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int kl = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
           const uint32_t sg = ksg[kl];
           float x = sacc[c][r] * cc;
           if (sg == (uint32_t)kSegInvalid) {
@@ -383,7 +429,7 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
       const int dr = 32 * dt + l32;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int ch = kh * (KW / 8) + 2 * s + hh;
+        const int ch = 2 * s + hh;
         const bf16x8 va = *(const bf16x8*)(vsb + vt_lds_byte(dr, ch));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
@@ -394,8 +440,8 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   // consumed, the next tile of the class streams into the other stage.
   auto run_pass = [&](auto general_tag) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
-    Cursor cu{-1, 0ull, -1, 0, 0.f};
-    Tile t_cur{-1, 0, 0.f}, t_nxt{-1, 0, 0.f}, t_nn{-1, 0, 0.f};
+    Cursor cu{-1, 0ull, 0, 0.f, 0};
+    Tile t_cur{-1, 0, 0.f, 0}, t_nxt{-1, 0, 0.f, 0}, t_nn{-1, 0, 0.f, 0};
     int cur = cursor_next(cu, !GENERAL, t_cur);
     if (cur < ntiles) {
       dma(t_cur.kb, ks0, vs0);
@@ -427,38 +473,9 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
   run_pass(std::false_type{});
   run_pass(std::true_type{});
 
-  // ---- combine lane halves, then key halves (sparse), then normalise
-  float l_tot = pair_sum(l_run);
-  if constexpr (KSPLIT == 2) {
-    // partner partials: row group 0 in ks0, row group 1 in ks1 ([DT*16][64] floats each)
-    static_assert(ROWG == 2 && DT * 16 * 64 * 4 <= TILE_ELEMS * 2, "merge buffers fit");
-    float* ox = (float*)(rg == 0 ? &ks0[0] : &ks1[0]);
-    float* ml = (float*)&vs0[0];  // [ROWG][2][64]
-    if (kh == 1) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ox[(dt * 16 + r) * 64 + lane] = oacc[dt][r];
-      ml[(rg * 2 + 0) * 64 + lane] = m_run;
-      ml[(rg * 2 + 1) * 64 + lane] = l_tot;
-    }
-    __syncthreads();
-    if (kh == 0) {
-      const float m1 = ml[(rg * 2 + 0) * 64 + lane];
-      const float l1 = ml[(rg * 2 + 1) * 64 + lane];
-      const float M = __builtin_elementwise_maximum(m_run, m1);
-      const float a0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-      const float a1 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          oacc[dt][r] = oacc[dt][r] * a0 + ox[(dt * 16 + r) * 64 + lane] * a1;
-      l_tot = l_tot * a0 + l1 * a1;
-      m_run = M;
-    }
-  }
-  if (kh == 0 && qvalid) {
+  // ---- combine lane halves, then normalise
+  const float l_tot = pair_sum(l_run);
+  if (qvalid) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t obase = ((int64_t)qrow * H + h) * D;
 #pragma unroll
@@ -483,13 +500,8 @@ __global__ __launch_bounds__(64 * ROWG * KSPLIT, 8 / (ROWG * KSPLIT)) void attn_
 
 template <int D, bool SPARSE, bool PEN>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t s) {
-  if (SPARSE) {
-    dim3 grid(a.nqb, a.H);
-    attn_bf16_kernel<D, 2, 2, true, PEN><<<grid, 256, 0, s>>>(a);
-  } else {
-    dim3 grid((a.nq + 255) / 256, a.H);
-    attn_bf16_kernel<D, 8, 1, false, PEN><<<grid, 512, 0, s>>>(a);
-  }
+  dim3 grid((a.nq + 255) / 256, a.H);
+  attn_bf16_kernel<D, SPARSE, PEN><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

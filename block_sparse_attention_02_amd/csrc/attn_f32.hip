@@ -18,6 +18,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float vsh[kSub][D];
   __shared__ uint32_t sgs[kSub];
   __shared__ float tss[kSub];
+  // sparse: the set of attended tiles (protected and routed) of this query block
+  __shared__ uint32_t tile_bits[SPARSE ? kBitmapWords : 1];
 
   const int lane = threadIdx.x;
   const int qblk = blockIdx.x;
@@ -41,20 +43,28 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const int nkb = (a.nk + 63) / 64;
-  int ntiles;
-  const int32_t* rt = nullptr;
-  if (SPARSE) {
-    ntiles = a.n_prot + a.k_sel;
-    rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
-  } else {
-    ntiles = nkb;
+  const int words = (nkb + 31) >> 5;
+  if constexpr (SPARSE) {
+    for (int i = lane; i < words; i += 64) tile_bits[i] = 0u;
+    __syncthreads();
+    const int32_t* rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
+    for (int i = lane; i < a.n_prot + a.k_sel; i += 64) {
+      const int kb = i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
+      if (kb >= 0 && kb < nkb) atomicOr(&tile_bits[kb >> 5], 1u << (kb & 31));
+    }
+    __syncthreads();
   }
 
-  for (int it = 0; it < ntiles; ++it) {
-    int kb = it;
-    if (SPARSE) kb = it < a.n_prot ? a.prot[it] : rt[it - a.n_prot];
-    kb = __builtin_amdgcn_readfirstlane(kb);
-    if (kb < 0 || kb >= nkb) continue;
+  // tiles in ascending order (sparse: only those in the set)
+  for (int kb = 0; kb < nkb; ++kb) {
+    if constexpr (SPARSE) {
+      const uint32_t w = tile_bits[kb >> 5] >> (kb & 31);
+      if (w == 0u) {  // nothing further in this word
+        kb = (kb | 31);
+        continue;
+      }
+      kb += __builtin_ctz(w);
+    }
     for (int sub = 0; sub < 64 / kSub; ++sub) {
       const int k0 = kb * 64 + sub * kSub;
       if (k0 >= a.nk) break;

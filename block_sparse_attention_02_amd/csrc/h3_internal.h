@@ -10,6 +10,10 @@ namespace h3 {
 constexpr int kTile = 64;         // key tile = routing block = 64 rows
 constexpr int kSegText = 0, kSegGuide = 1, kSegAudio = 2, kSegOutput = 3;
 constexpr int kSegInvalid = 255;  // marks key slots past the end of a tile
+// Largest sequence the router and the block-sparse kernels accept, in 64-row blocks
+// (896,000 rows); their per-workgroup tile bitmaps in LDS are sized for it.
+constexpr int kMaxBlocks = 14000;
+constexpr int kBitmapWords = (kMaxBlocks + 31) / 32;
 
 // Per 64-key tile summary (see tile_info_kernel).
 constexpr int kTileAnyGuide = 1, kTileUniformGuide = 2, kTileFull = 4;

@@ -303,7 +303,7 @@ RouterWs router_ws_carve(void* ws, int n, int H, int D) {
 }
 
 // Largest block count the score/top-k kernel keeps in LDS (QB x nb floats).
-int router_max_blocks() { return 14000; }
+int router_max_blocks() { return kMaxBlocks; }
 
 hipError_t launch_router(const void* q, const void* k, bool bf16, int n, int H, int D,
                          const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,

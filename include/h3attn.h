@@ -137,15 +137,16 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
 /*
  * Block-sparse attention over routed tiles.
  * From "H3 SLA Attention", "How it works" and inputs table: query block qb of
- * head h attends the keys of its protected blocks prot[0..n_prot) and its
- * routed blocks tiles[h][qb][0..k_sel) (entries < 0 are skipped) and nothing
- * else (a hard zero, no tail term). Inside those tiles the score is the dense
- * TARA score of attn_dense_tara, so the penalty applies to routed guide tiles
- * of output-video queries when strength > 0 and cap > 0.
+ * head h attends the keys of the set of blocks formed by its protected blocks
+ * prot[0..n_prot) and its routed blocks tiles[h][qb][0..k_sel), and nothing
+ * else (a hard zero, no tail term). Entries outside [0, ceil(n/64)) are
+ * skipped and a block listed more than once counts once. Inside those tiles the
+ * score is the dense TARA score of attn_dense_tara, so the penalty applies to
+ * routed guide tiles of output-video queries when strength > 0 and cap > 0.
  * Workspace: attn_block_sparse_workspace(n, heads, head_dim, dtype) bytes.
  * Errors: as attn_dense_tara, plus H3_EINVAL for k_sel < 0, n_prot < 0,
  * n_prot + k_sel == 0, null tiles (k_sel > 0) or prot (n_prot > 0);
- * H3_EUNSUPPORTED for block_size != 64.
+ * H3_EUNSUPPORTED for block_size != 64 or more than 14,000 blocks.
  */
 size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype);
 int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,

@@ -20,13 +20,15 @@ def block_sparse_block(q_h, k_h, v_h, seg, t, params, scale, block_size, prot, t
 
     q_h, k_h, v_h: [n, d] float64. ``prot``: protected block indices;
     ``tiles_row``: routed block indices of this (head, query block); entries
-    below zero are ignored. The keys are the rows of every protected and
-    routed block; the softmax runs over those keys only, with the dense TARA
-    score s_ij = scale * q_i . k_j - p_ij. Returns (o [rows, d], lse [rows]).
+    outside the sequence's blocks are ignored. The keys are the rows of the set
+    of protected and routed blocks (a block listed twice counts once); the
+    softmax runs over those keys only, with the dense TARA score
+    s_ij = scale * q_i . k_j - p_ij. Returns (o [rows, d], lse [rows]).
     """
     n = q_h.shape[0]
+    nb = (n + block_size - 1) // block_size
     lo, hi = qb * block_size, min(n, (qb + 1) * block_size)
-    blocks = [int(b) for b in list(prot) + list(tiles_row) if int(b) >= 0]
+    blocks = sorted({int(b) for b in list(prot) + list(tiles_row) if 0 <= int(b) < nb})
     if not blocks:
         return np.zeros((hi - lo, q_h.shape[1])), np.full(hi - lo, -np.inf)
     keys = np.concatenate([np.arange(b * block_size, min(n, (b + 1) * block_size))

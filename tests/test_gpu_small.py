@@ -255,6 +255,38 @@ def test_sparse_with_penalty_small(sparsity):
     compare(o, lse, o_ref, l_ref, "bf16", f"sparse pen s={sparsity}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
+def test_sparse_hand_built_lists(d, dtype):
+    """Arbitrary tile lists: each block's own random tiles (so the four blocks that
+    share a workgroup attend different sets), repeated entries, -1, an index one past
+    the last block and a protected block listed again. Every output row against the
+    oracle, which takes the listed blocks as a set; the last workgroup holds fewer
+    than four query blocks."""
+    wl = _ragged(d, dtype, 95, heads=2)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    nb = (wl.n + 63) // 64
+    rng = np.random.default_rng(95)
+    tiles = rng.integers(-1, nb + 1, size=(2, nb, 6)).astype(np.int32)
+    tiles[:, :, 5] = tiles[:, :, 0]          # a repeated entry in every list
+    tiles[0, 2, 1] = 3                        # a protected block listed again
+    prot = np.array([0, 3, 3], dtype=np.int32)
+    print(f"case hand lists d={d} {dtype} n={wl.n} nb={nb}", flush=True)
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d,
+                                   torch.tensor(tiles, device="cuda"),
+                                   torch.tensor(prot, device="cuda"), *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, 64, prot, tiles)
+    o_ref = np.zeros((wl.n, 2, d))
+    l_ref = np.zeros((wl.n, 2))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * 64:qb * 64 + len(ob), h] = ob
+        l_ref[qb * 64:qb * 64 + len(ob), h] = lb
+    compare(o, lse, o_ref, l_ref, dtype, f"sparse hand lists d={d} {dtype}")
+
+
 # ------------------------------------------------------------------- merge
 
 def test_lse_merge_matches_oracle():

@@ -447,6 +447,22 @@ def test_sparse_brute_force_tiny():
             assert np.max(np.abs(ob - ref_o)) < 1e-12 and np.max(np.abs(lb - ref_l)) < 1e-12
 
 
+def test_sparse_listed_blocks_form_a_set():
+    """Repeated, protected-again and out-of-range entries do not change the key set."""
+    wl, seg, t, q, k, v = _sparse_case(seed=303)
+    n = wl.n
+    nb = (n + 15) // 16
+    prot = np.array([0, 2])
+    messy = np.array([5, 5, 2, -1, nb, 9, 5])
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    ob, lb = oracle.block_sparse_block(q64[:, 1], k64[:, 1], v64[:, 1], seg, t, wl.tara,
+                                       wl.scale, 16, prot, messy, 1)
+    keys = np.array([r for b in (0, 2, 5, 9) for r in range(16 * b, 16 * b + 16) if r < n])
+    ref_o, ref_l = _brute_dense_rows(q64[:, 1], k64[:, 1], v64[:, 1], seg, t, wl.tara,
+                                    wl.scale, range(16, 32), keys)
+    assert np.max(np.abs(ob - ref_o)) < 1e-12 and np.max(np.abs(lb - ref_l)) < 1e-12
+
+
 def _brute_dense_rows(q, k, v, seg, t, params, scale, rows, keys):
     strength, window, falloff, cap = params
     o = np.zeros((len(rows), q.shape[1]))
