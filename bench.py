@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/call + dense-equiv TFLOP/s (%MFMA peak), 116,883 rows x 56 heads, 1 GPU"
-DENSE_KERNEL = "attn_bf16_kernel<128, 8, 1, false, true>"
+DENSE_KERNEL = "attn_bf16_kernel<128, false, true>"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_dense_tara_116883x56_pmc.json")
 
 
@@ -96,7 +96,7 @@ def _counter_kib(path, counter, kernel_substr):
 
 def pmc_summary(dirs):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
-    kern = "attn_bf16_kernel<128, 8, 1, false, true>"
+    kern = DENSE_KERNEL
     copy_kern = "copyBuffer"
     f_kib, nf = _counter_kib(fetch_dir, "FETCH_SIZE", kern)
     w_kib, nw = _counter_kib(write_dir, "WRITE_SIZE", kern)
