@@ -21,9 +21,10 @@
 // Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
 // lane holds one query column; softmax row reductions stay in registers plus one
 // exchange between lane halves.
-// K and V^T tiles are double-buffered in LDS with an XOR swizzle on 16-byte chunks
-// (bank-conflict-free operand reads) and loaded one tile ahead straight from global
-// memory into LDS (global_load_lds_dwordx4), so the loads hold no registers.
+// K and V^T tiles are double-buffered in LDS in rows padded by 16 bytes (bank-conflict-
+// free operand reads, and every operand address is one base register plus an immediate)
+// and loaded ahead straight from global memory into LDS (buffer_load ... lds), so the
+// loads hold no registers.
 // V^T comes from a transposed copy of v whose keys are permuted within 16-key groups
 // (bits 2 and 3 of the key index swapped) so that the probability registers produced by
 // the first product are directly the B operand of the second.
@@ -47,6 +48,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Running maxima are only raised when a tile exceeds them by more than this (log2
 // units); probabilities then stay below 2^8 and most tiles skip the O rescale.
 constexpr float kLazyRescale = 8.0f;
+constexpr float kRescaleSum = 256.0f;  // 2^kLazyRescale
 // Buffer descriptor word 3 for raw 32-bit-format loads on CDNA (out-of-range reads
 // return zero).
 constexpr int kBufferFlags = 0x00020000;
@@ -56,9 +58,6 @@ __host__ __device__ constexpr int key_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
-// Lanes l and l^32 hold the two key halves of the same query column.
-__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
 // One 16-byte chunk per lane from a raw buffer [base, base + nbytes) straight into LDS
 // at lds + 16 * lane (the LDS address is wave-uniform); out-of-range lanes read zero.
@@ -137,19 +136,54 @@ __global__ __launch_bounds__(64) void tile_info_kernel(const uint8_t* __restrict
 }
 
 // ------------------------------------------------------------------ attention
-// LDS layouts (bf16, 16-byte chunks, XOR-swizzled so that every 8- and 16-lane phase
-// of a 128-bit operand read touches distinct banks):
-//   K   : row = key (D*2 bytes); chunk c of key r sits at chunk c ^ (r & 15) (D = 128)
-//         or c ^ (r & 7) (D = 64).
-//   V^T : rows d and d+1 share a 256-byte line p = d/2; chunk c of row d sits at
-//         (8*(d&1) + c) ^ ((p & 15) ^ 4*(d&1)).
+// LDS layouts (bf16): rows padded by one 16-byte slot, so 16 consecutive rows read at
+// the same column start on 16 distinct bank groups (row stride = 16 bytes mod 256):
+//   K   : row = key, D*2 + 16 bytes per row;
+//   V^T : row = d, 64 keys = 128 + 16 bytes per row.
+// A tile is filled by 1 KB direct-to-LDS wave loads over its contiguous bytes; lanes that
+// land on a pad slot read out of range (zero).
 template <int D>
-__device__ __forceinline__ int k_lds_chunk(int r, int c) {
-  return D == 128 ? (c ^ (r & 15)) : (c ^ (r & 7));
+struct Lds {
+  static constexpr int KRS = D * 2 + 16;   // K row stride (bytes)
+  static constexpr int KSL = D / 8 + 1;    // 16-byte slots per K row
+  static constexpr int VRS = 128 + 16;     // V^T row stride (bytes)
+  static constexpr int VSL = 9;            // 16-byte slots per V^T row
+  static constexpr int KBYTES = 64 * KRS;  // one K tile
+  static constexpr int VBYTES = D * VRS;   // one V^T tile
+  static constexpr int KINS = KBYTES / 1024;  // 1 KB wave loads per K tile
+  static constexpr int VINS = VBYTES / 1024;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole wave loads");
+};
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset that reads zero
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitAll0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
+
+// Workgroup barrier without the memory-model fence of __syncthreads (that fence would
+// also wait for the direct-to-LDS loads meant to stay in flight across it). WAIT is
+// the s_waitcnt the caller needs before arriving; the empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+template <int WAIT>
+__device__ __forceinline__ void slot_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ int vt_lds_byte(int d, int c) {
-  const int p = d >> 1, b = d & 1;
-  return p * 256 + (((8 * b + c) ^ ((p & 15) ^ (4 * b))) * 16);
+
+// Lanes l and l^32 hold the two key halves of the same query column; one
+// v_permlane32_swap gives every lane both halves.
+__device__ __forceinline__ float pair_max_swap(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum_swap(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, bool SPARSE, bool PEN>
@@ -157,30 +191,31 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NW = 8;               // waves per workgroup (two per SIMD)
   constexpr int BM = 32 * NW;         // query rows per workgroup
   constexpr int QB = BM / kTile;      // query blocks per workgroup (sparse)
-  constexpr int KW = 64;              // keys of a tile handled by one wave
-  constexpr int NT = KW / 32;         // 32x32 score tiles per wave
-  constexpr int NS = KW / 16;         // k-steps of the PV product
+  constexpr int NT = 2;               // 32x32 score tiles per wave (64 keys)
+  constexpr int NS = 4;               // k-steps of the PV product (64 keys / 16)
   constexpr int DK = D / 16;          // k-steps of the QK product
   constexpr int DT = D / 32;          // 32-row output tiles (over d)
-  constexpr int TILE_ELEMS = 64 * D;  // bf16 elements of one K (or V^T) tile
-  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / NW;  // 1 KB wave loads per wave
-  constexpr int KROW_BYTES = D * 2;
+  using L = Lds<D>;
+  constexpr int KDMA = (L::KINS + NW - 1) / NW;  // wave loads per wave and K tile (at most)
+  constexpr int VDMA = (L::VINS + NW - 1) / NW;
 
-  // Two stages, each its own LDS object so the compiler can tell the stage being
-  // read from the stage being filled by the direct-to-LDS loads.
-  __shared__ __attribute__((aligned(1024))) uint16_t ks0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t ks1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs1[TILE_ELEMS];
-  __shared__ uint8_t kseg0[64], kseg1[64];
-  __shared__ float kt0[64], kt1[64];
+  // Three stages each for K and V^T, each stage its own LDS object so the compiler can
+  // tell the stage being read from the stage being filled by the direct-to-LDS loads.
+  __shared__ __attribute__((aligned(1024))) uint16_t ks0[L::KBYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks1[L::KBYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t ks2[L::KBYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs0[L::VBYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs1[L::VBYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs2[L::VBYTES / 2];
+  __shared__ uint8_t kseg0[64], kseg1[64], kseg2[64];
+  __shared__ float kt0[64], kt1[64], kt2[64];
+  __shared__ int simd_waves[4];
   // sparse: bitmap 0 = protected tiles, bitmap 1 + j = routed tiles of query block j
   __shared__ uint32_t tile_bits[SPARSE ? (QB + 1) * kBitmapWords : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rg = wave;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int qblk = blockIdx.x;
@@ -192,7 +227,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   const TileInfo* __restrict__ tinfo = a.tinfo;
   const float c_log2 = a.scale * kLog2e;
 
-  const int qrow = qblk * BM + rg * 32 + l32;
+  const int qrow = qblk * BM + wave * 32 + l32;
   const bool qvalid = qrow < a.nq;
   bf16x8 qreg[DK];
 #pragma unroll
@@ -206,8 +241,18 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   }
   const float qt = qvalid ? a.q_t[qrow] : 0.f;
   const bool q_out = PEN && qvalid && a.q_seg[qrow] == kSegOutput;
-  // does any query row of this workgroup take the penalty?
-  const bool pen_wg = PEN && __syncthreads_or(q_out);
+
+  // ---- the two waves that share a SIMD take opposite phases (group 0 / group 1):
+  // while one runs its matrix-core slot the other runs its softmax slot.
+  if (tid < 4) simd_waves[tid] = 0;
+  // does any query row of this workgroup take the penalty? (also orders the reset above)
+  const bool pen_wg = __syncthreads_or(q_out);
+  int grp = 0;
+  if (lane == 0) {
+    const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);  // HW_ID.SIMD_ID
+    grp = atomicAdd(&simd_waves[simd & 3], 1) & 1;
+  }
+  const bool grp_b = __builtin_amdgcn_readfirstlane(grp) != 0;
 
   const int nkb = (a.nk + 63) / 64;
   const int ntiles = nkb;  // tiles are visited in ascending order; the cursor skips
@@ -215,7 +260,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   // query blocks of this workgroup that exist (bit j = block QB*qblk + j)
   int qb_valid = 0;
   // this wave's bit in a tile's attend mask
-  const int my_qbit = 1 << (rg * 32 / kTile);
+  const int my_qbit = 1 << (wave * 32 / kTile);
   if constexpr (SPARSE) {
     const int words = (nkb + 31) >> 5;  // the cursor reads no word past these
     for (int i = tid; i < (QB + 1) * words; i += 64 * NW)
@@ -241,32 +286,40 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // ---- per-lane byte offsets of this thread's DMA chunks inside a tile (fixed)
-  uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
+  // ---- per-lane global byte offsets of this thread's wave loads (wave load i of a tile
+  // belongs to wave i % 8)
+  uint32_t koff[KDMA], voff[VDMA];
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int off = (wave * DMA_PER_WAVE + i) * 1024 + lane * 16;  // LDS byte offset
-    const int r = off / KROW_BYTES, pc = (off % KROW_BYTES) / 16;    // key row, chunk slot
-    koff[i] = (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)(k_lds_chunk<D>(r, pc) * 16);
-    // invert the V^T layout: slot -> (row d, logical chunk c)
-    const int p = off / 256, slot = (off % 256) / 16;
-    const int b = ((slot ^ (p & 15)) >> 3) & 1;
-    const int c = (slot ^ ((p & 15) ^ (4 * b))) & 7;
-    voff[i] = (uint32_t)(2 * p + b) * (uint32_t)(a.nkp * 2) + (uint32_t)(c * 16);
+  for (int j = 0; j < KDMA; ++j) {
+    const int slot = (wave + NW * j) * 64 + lane;
+    const int r = slot / L::KSL, c = slot % L::KSL;
+    koff[j] = c == L::KSL - 1 ? kOutOfRange
+                              : (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)(c * 16);
   }
-  auto dma = [&](int kb, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+#pragma unroll
+  for (int j = 0; j < VDMA; ++j) {
+    const int slot = (wave + NW * j) * 64 + lane;
+    const int d = slot / L::VSL, c = slot % L::VSL;
+    voff[j] = c == L::VSL - 1 ? kOutOfRange
+                              : (uint32_t)d * (uint32_t)(a.nkp * 2) + (uint32_t)(c * 16);
+  }
+  auto dma_k = [&](int kb, uint16_t* kdst) __attribute__((always_inline)) {
     const int k0 = kb * 64;
     const int rows = min(64, a.nk - k0);
     const void* kbase = kp + ((int64_t)k0 * H + h) * D;
     const int kbytes = (rows - 1) * H * D * 2 + D * 2;
-    const void* vbase = vtp + (int64_t)h * D * a.nkp + k0;
+#pragma unroll
+    for (int j = 0; j < KDMA; ++j)
+      if (wave + NW * j < L::KINS)
+        buffer_to_lds16(kbase, kbytes, (char*)kdst + (wave + NW * j) * 1024, koff[j]);
+  };
+  auto dma_v = [&](int kb, uint16_t* vdst) __attribute__((always_inline)) {
+    const void* vbase = vtp + (int64_t)h * D * a.nkp + kb * 64;
     const int vbytes = (D - 1) * a.nkp * 2 + 128;
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_to_lds16(kbase, kbytes, kdst + (wave * DMA_PER_WAVE + i) * 512, koff[i]);
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_to_lds16(vbase, vbytes, vdst + (wave * DMA_PER_WAVE + i) * 512, voff[i]);
+    for (int j = 0; j < VDMA; ++j)
+      if (wave + NW * j < L::VINS)
+        buffer_to_lds16(vbase, vbytes, (char*)vdst + (wave + NW * j) * 1024, voff[j]);
   };
   // row segment ids and times of a tile (per-key tiles only)
   uint32_t sreg = kSegInvalid;
@@ -293,17 +346,20 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     return (flags & kTileFull) &&
            (!pen_wg || !(flags & kTileAnyGuide) || (flags & kTileUniformGuide));
   };
-  // Walks the tile list in order, yielding the entries of one class. Each wave reads
-  // 64 entries at a time and keeps a ballot mask of the matching ones.
   // Walks the key tiles in ascending order, yielding those of one class that some
   // wave attends. Each wave examines 64 tiles at a time and keeps a ballot mask of
-  // the matching ones; .qmask says which query blocks attend the tile (sparse).
+  // the matching ones; .qmask says which query blocks attend the tile (sparse). Every
+  // wave walks the same sequence.
   struct Cursor { int chunk; uint64_t mask; int flags_lane; float t_lane; int qm_lane; };
   struct Tile { int kb; int flags; float t; int qmask; };
-  auto cursor_next = [&](Cursor& cu, bool want_fast, Tile& tl) __attribute__((always_inline)) -> int {
+  auto cursor_next = [&](Cursor& cu, bool want_fast, Tile& tl) __attribute__((always_inline)) {
     while (cu.mask == 0ull) {
       ++cu.chunk;
-      if (cu.chunk * 64 >= ntiles) return ntiles;
+      if (cu.chunk * 64 >= ntiles) {
+        tl.kb = ntiles;
+        tl.qmask = 0;
+        return;
+      }
       const int kb = cu.chunk * 64 + lane;
       int qm = 0;
       TileInfo ti{0, 0.f};
@@ -334,7 +390,10 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     tl.flags = __builtin_amdgcn_readfirstlane(__shfl(cu.flags_lane, bit));
     tl.t = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__shfl(cu.t_lane, bit))));
     tl.qmask = SPARSE ? __builtin_amdgcn_readfirstlane(__shfl(cu.qm_lane, bit)) : 1;
-    return tl.kb;
+  };
+  // does this wave compute tile tl?
+  auto attends = [&](const Tile& tl) __attribute__((always_inline)) -> bool {
+    return tl.kb < ntiles && (!SPARSE || (tl.qmask & my_qbit));
   };
 
   f32x16 oacc[DT];
@@ -344,38 +403,106 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m_run = -INFINITY;
   float l_run = 0.f;
+  f32x16 sacc[NT];    // scores of the tile between its QK product and its softmax
+  bf16x8 pb[NS];      // probabilities of the tile between its softmax and its PV product
 
-  // ---- one tile: S^T = K Q^T, scores with the penalty, online softmax, O^T += V^T P^T.
-  auto tile_body = [&](auto general_tag, const uint16_t* kst, const uint16_t* vst,
-                       const uint8_t* ksg, const float* ktt, const Tile& tl) __attribute__((always_inline)) {
-    constexpr bool GENERAL = decltype(general_tag)::value;
-    if (SPARSE && !(tl.qmask & my_qbit)) return;  // this wave's block skips the tile
-    f32x16 sacc[NT];
+  // ---- matrix-core slot: O^T += V^T P^T for the previous tile, then S^T = K Q^T.
+  auto mfma_slot = [&](const uint16_t* kst, const uint16_t* vst, bool do_pv, bool do_qk)
+      __attribute__((always_inline)) {
+    if (do_pv) {
+      const char* vsb = (const char*)vst + l32 * L::VRS + hh * 16;
 #pragma unroll
-    for (int c = 0; c < NT; ++c)
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DK; ++s) {
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        const int kr = 32 * c + l32;
-        const bf16x8 ka = *(const bf16x8*)&kst[kr * D + k_lds_chunk<D>(kr, 2 * s + hh) * 8];
-        sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 va = *(const bf16x8*)(vsb + dt * 32 * L::VRS + s * 32);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
+        }
       }
     }
-    float cc = c_log2, bb = 0.f, tmax;
-    if constexpr (!GENERAL) {
-      if (PEN && pen_wg && (tl.flags & kTileUniformGuide) && q_out)
-        bb = -tara_pen(fabsf(qt - tl.t), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
-      float mx = -INFINITY;
+    // keep the two products apart so their operand reads do not pile up in registers
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) {
 #pragma unroll
       for (int c = 0; c < NT; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2)
-          mx = __builtin_elementwise_maximum(
-              __builtin_elementwise_maximum(mx, sacc[c][r]), sacc[c][r + 1]);
-      tmax = mx * cc + bb;
+        for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
+      const char* ksb = (const char*)kst + l32 * L::KRS + hh * 16;
+#pragma unroll
+      for (int s = 0; s < DK; ++s) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const bf16x8 ka = *(const bf16x8*)(ksb + c * 32 * L::KRS + s * 32);
+          sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- softmax slot: scores with the penalty, online softmax, probabilities in bf16.
+  // p = exp2(s * cc + mb) for the 32 scores of this lane, as bf16 into pb; returns
+  // the float32 sum of the 32 (four chains).
+  auto exp_tile = [&](float cc, float mb) __attribute__((always_inline)) -> float {
+    float r[4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      f32x8 pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
+        r[e & 3] = (s == 0 && e < 4) ? pv[e] : r[e & 3] + pv[e];
+      }
+      pb[s] = __builtin_convertvector(pv, bf16x8);
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
+  };
+  // Raises the running maximum to cover this tile's scaled maximum `tmax` (log2 units,
+  // equal in both lane halves), rescaling O and the running sum.
+  auto raise_max = [&](float tmax) __attribute__((always_inline)) {
+    const float m_new = __builtin_elementwise_maximum(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  };
+  // maximum of this lane's 32 scores (a tree of three-input maxima)
+  auto score_max = [&]() __attribute__((always_inline)) -> float {
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i >> 2, r = 4 * (i & 3);
+      m[i] = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(sacc[c][r], sacc[c][r + 1]),
+          __builtin_elementwise_maximum(sacc[c][r + 2], sacc[c][r + 3]));
+    }
+    return __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[0], m[1]),
+                                      __builtin_elementwise_maximum(m[2], m[3])),
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[4], m[5]),
+                                      __builtin_elementwise_maximum(m[6], m[7])));
+  };
+
+  // ---- softmax slot: scores with the penalty, online softmax, probabilities in bf16.
+  // Fast tiles are exponentiated against the running maximum straight away; only if a
+  // lane's sum of the 32 exceeds 2^8 (so some probability might, or the maximum is still
+  // -inf) does the tile take the maximum, rescale and exponentiate again. Probabilities
+  // thus stay at most 2^8 while most tiles skip the maximum altogether.
+  auto softmax_slot = [&](auto general_tag, const uint8_t* ksg, const float* ktt,
+                          const Tile& tl) __attribute__((always_inline)) {
+    constexpr bool GENERAL = decltype(general_tag)::value;
+    if constexpr (!GENERAL) {
+      float bb = 0.f;
+      if (PEN && pen_wg && (tl.flags & kTileUniformGuide) && q_out)
+        bb = -tara_pen(fabsf(qt - tl.t), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
+      float rs = exp_tile(c_log2, bb - m_run);
+      if (__ballot(!(rs <= kRescaleSum)) != 0ull) {
+        raise_max(pair_max_swap(score_max() * c_log2 + bb));
+        rs = exp_tile(c_log2, bb - m_run);
+      }
+      l_run += rs;
     } else {
       float mx = -INFINITY;
 #pragma unroll
@@ -384,7 +511,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int kl = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
           const uint32_t sg = ksg[kl];
-          float x = sacc[c][r] * cc;
+          float x = sacc[c][r] * c_log2;
           if (sg == (uint32_t)kSegInvalid) {
             x = -INFINITY;
           } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
@@ -395,86 +522,77 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
           mx = __builtin_elementwise_maximum(mx, x);
         }
       }
-      cc = 1.f;
-      tmax = mx;
-    }
-    tmax = pair_max(tmax);
-    if (__ballot(tmax > m_run + kLazyRescale) != 0ull) {
-      const float m_new = __builtin_elementwise_maximum(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float mb = bb - (m_run == -INFINITY ? 0.f : m_run);
-    bf16x8 pb[NS];
-    float rs0 = 0.f, rs1 = 0.f;  // float32 row sums (two chains)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      f32x8 pv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
-        if (e & 1) rs1 += pv[e]; else rs0 += pv[e];
-      }
-      pb[s] = __builtin_convertvector(pv, bf16x8);
-    }
-    l_run += rs0 + rs1;
-    const char* vsb = (const char*)vst;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dr = 32 * dt + l32;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int ch = 2 * s + hh;
-        const bf16x8 va = *(const bf16x8*)(vsb + vt_lds_byte(dr, ch));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
-      }
+      const float tmax = pair_max_swap(mx);
+      if (__ballot(tmax > m_run + kLazyRescale) != 0ull) raise_max(tmax);
+      l_run += exp_tile(1.f, m_run == -INFINITY ? 0.f : -m_run);
     }
   };
 
-  // ---- one pass over the tiles of one class, double-buffered: while stage s is
-  // consumed, the next tile of the class streams into the other stage.
+  // ---- one pass over the tiles of one class. Every wave runs the same sequence of
+  // slots separated by workgroup barriers: matrix slot j (O += P_{j-1} V_{j-1}, then
+  // S_j = Q K_j^T), softmax slot j (issue the loads of K_{j+2} and V_{j+1}, then the
+  // softmax of S_j). Group 1 passes one extra barrier before its first slot and group 0
+  // one after its last, so group 1 runs one slot behind group 0 and each SIMD overlaps
+  // one wave's matrix products with the other wave's softmax. K_j sits in stage j % 3 and
+  // V_j in stage j % 3: with the one-slot skew, a stage is refilled only after both groups
+  // have finished reading it, and every load has two slots to land.
   auto run_pass = [&](auto general_tag) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
     Cursor cu{-1, 0ull, 0, 0.f, 0};
-    Tile t_cur{-1, 0, 0.f, 0}, t_nxt{-1, 0, 0.f, 0}, t_nn{-1, 0, 0.f, 0};
-    int cur = cursor_next(cu, !GENERAL, t_cur);
-    if (cur < ntiles) {
-      dma(t_cur.kb, ks0, vs0);
-      if (GENERAL) { small_load(t_cur.kb); small_store(kseg0, kt0); }
+    Tile tp{ntiles, 0, 0.f, 0}, tq{ntiles, 0, 0.f, 0}, tn{ntiles, 0, 0.f, 0};
+    cursor_next(cu, !GENERAL, tq);
+    if (tq.kb >= ntiles) return;
+    cursor_next(cu, !GENERAL, tn);
+    // prologue: K_0, K_1, V_0 (and the key rows of tiles 0 and 1)
+    dma_k(tq.kb, ks0);
+    dma_v(tq.kb, vs0);
+    if (GENERAL) small_load(tq.kb);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (GENERAL) small_store(kseg0, kt0);
+    if (tn.kb < ntiles) {
+      dma_k(tn.kb, ks1);
+      if (GENERAL) small_load(tn.kb);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (GENERAL) small_store(kseg1, kt1);
     }
-    __syncthreads();
-    while (cur < ntiles) {
-      const int nxt = cursor_next(cu, !GENERAL, t_nxt);
-      if (nxt < ntiles) {
-        dma(t_nxt.kb, ks1, vs1);
-        if (GENERAL) small_load(t_nxt.kb);
+    slot_barrier<kWaitAll0>();
+    if (grp_b) slot_barrier<kWaitAll0>();
+    // One (matrix, softmax) slot pair; the stage arguments rotate with j % 3.
+    auto step = [&](uint16_t* kcur, uint16_t* vprev, uint16_t* knn, uint16_t* vnext,
+                    uint8_t* sgcur, float* ttcur, uint8_t* sgnext, float* ttnext)
+        __attribute__((always_inline)) {
+      mfma_slot(kcur, vprev, attends(tp), attends(tq));
+      // the key rows of tile j+1 were fetched during the previous softmax slot
+      if (GENERAL && tn.kb < ntiles) small_store(sgnext, ttnext);
+      slot_barrier<kWaitAll0>();
+      Tile tnn;
+      cursor_next(cu, !GENERAL, tnn);
+      if (tnn.kb < ntiles) {
+        dma_k(tnn.kb, knn);
+        if (GENERAL) small_load(tnn.kb);
       }
-      tile_body(general_tag, ks0, vs0, kseg0, kt0, t_cur);
-      if (GENERAL && nxt < ntiles) small_store(kseg1, kt1);
-      __syncthreads();
-      if (nxt >= ntiles) break;
-      const int nn = cursor_next(cu, !GENERAL, t_nn);
-      if (nn < ntiles) {
-        dma(t_nn.kb, ks0, vs0);
-        if (GENERAL) small_load(t_nn.kb);
-      }
-      tile_body(general_tag, ks1, vs1, kseg1, kt1, t_nxt);
-      if (GENERAL && nn < ntiles) small_store(kseg0, kt0);
-      __syncthreads();
-      cur = nn;
-      t_cur = t_nn;
+      if (tn.kb < ntiles) dma_v(tn.kb, vnext);
+      if (attends(tq)) softmax_slot(general_tag, sgcur, ttcur, tq);
+      slot_barrier<kWaitLgkm0>();
+      tp = tq;
+      tq = tn;
+      tn = tnn;
+    };
+    while (true) {
+      step(ks0, vs2, ks2, vs1, kseg0, kt0, kseg1, kt1);
+      if (tp.kb >= ntiles) break;
+      step(ks1, vs0, ks0, vs2, kseg1, kt1, kseg2, kt2);
+      if (tp.kb >= ntiles) break;
+      step(ks2, vs1, ks1, vs0, kseg2, kt2, kseg0, kt0);
+      if (tp.kb >= ntiles) break;
     }
+    if (!grp_b) slot_barrier<kWaitAll0>();
   };
   run_pass(std::false_type{});
   run_pass(std::true_type{});
 
   // ---- combine lane halves, then normalise
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = pair_sum_swap(l_run);
   if (qvalid) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t obase = ((int64_t)qrow * H + h) * D;
