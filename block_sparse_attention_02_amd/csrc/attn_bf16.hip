@@ -387,9 +387,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     const int bit = __builtin_ctzll(cu.mask);
     cu.mask &= cu.mask - 1;
     tl.kb = cu.chunk * 64 + bit;
-    tl.flags = __builtin_amdgcn_readfirstlane(__shfl(cu.flags_lane, bit));
-    tl.t = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__shfl(cu.t_lane, bit))));
-    tl.qmask = SPARSE ? __builtin_amdgcn_readfirstlane(__shfl(cu.qm_lane, bit)) : 1;
+    tl.flags = __builtin_amdgcn_readlane(cu.flags_lane, bit);
+    tl.t = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t_lane), bit));
+    tl.qmask = SPARSE ? __builtin_amdgcn_readlane(cu.qm_lane, bit) : 1;
   };
   // does this wave compute tile tl?
   auto attends = [&](const Tile& tl) __attribute__((always_inline)) -> bool {
