@@ -112,8 +112,10 @@ __global__ __launch_bounds__(256) void vt_transpose_kernel(const uint16_t* __res
 }
 
 // ------------------------------------------------------------------ tile info
-// Per 64-key tile: bit0 any guide key, bit1 every key a guide row of one frame,
-// bit2 all 64 keys present; .t = time of the tile's first key.
+// Per 64-key tile: bit0 any guide key, bit1 every key a guide row of one frame, bit2 all
+// 64 keys present, bit3 the 64 keys form exactly two runs of equal (segment, time), with
+// bit4/bit5 marking which run is guide video, bits 8-15 the first key of the second run;
+// .t = time of the first key, .t2 = time of the second run.
 __global__ __launch_bounds__(64) void tile_info_kernel(const uint8_t* __restrict__ k_seg,
                                                        const float* __restrict__ k_t, int nk,
                                                        TileInfo* __restrict__ info) {
@@ -126,12 +128,25 @@ __global__ __launch_bounds__(64) void tile_info_kernel(const uint8_t* __restrict
   const uint64_t full = __ballot(valid);
   const float t0 = __shfl(tt, 0);
   const uint64_t same = __ballot(tt == t0);
+  // lanes where (segment, time) differs from the previous key
+  const uint32_t sg_prev = __shfl_up(sg, 1);
+  const float t_prev = __shfl_up(tt, 1);
+  const uint64_t change = __ballot(threadIdx.x > 0 && (sg != sg_prev || tt != t_prev));
+  const int split = change ? __builtin_ctzll(change) : 64;
+  const float t2 = __shfl(tt, split & 63);
   if (threadIdx.x == 0) {
     int f = 0;
     if (g) f |= kTileAnyGuide;
     if (g == ~0ull && same == ~0ull) f |= kTileUniformGuide;
-    if (full == ~0ull) f |= kTileFull;
-    info[kb] = TileInfo{f, t0};
+    if (full == ~0ull) {
+      f |= kTileFull;
+      if (__popcll(change) == 1) {
+        f |= kTileTwoRun;
+        if (g & 1ull) f |= kTileGuideA;
+        if ((g >> split) & 1ull) f |= kTileGuideB;
+      }
+    }
+    info[kb] = TileInfo{f | (split << 8), t0, t2, 0};
   }
 }
 
@@ -348,21 +363,32 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   };
   // Walks the key tiles in ascending order, yielding those of one class that some
   // wave attends. Each wave examines 64 tiles at a time and keeps a ballot mask of
-  // the matching ones; .qmask says which query blocks attend the tile (sparse). Every
-  // wave walks the same sequence.
-  struct Cursor { int chunk; uint64_t mask; int flags_lane; float t_lane; int qm_lane; };
-  struct Tile { int kb; int flags; float t; int qmask; };
-  auto cursor_next = [&](Cursor& cu, bool want_fast, Tile& tl) __attribute__((always_inline)) {
+  // the matching ones; .qmask says which query blocks attend the tile (sparse). Sparse
+  // launches load the summaries of the next 64 tiles one refill ahead, so a refill does
+  // not wait on memory. Every wave walks the same sequence.
+  struct Cursor {
+    int chunk; uint64_t mask; int flags_lane; float t_lane; float t2_lane; int qm_lane;
+    TileInfo pre;
+  };
+  struct Tile { int kb; int flags; float t; int qmask; float t2; int split; };
+  auto cursor_start = [&]() __attribute__((always_inline)) -> Cursor {
+    TileInfo pre{64 << 8, 0.f, 0.f, 0};
+    if (SPARSE && lane < nkb) pre = tinfo[lane];
+    return Cursor{-1, 0ull, 0, 0.f, 0.f, 0, pre};
+  };
+  auto cursor_next = [&](Cursor& cu, bool want_fast) __attribute__((always_inline)) -> Tile {
     while (cu.mask == 0ull) {
       ++cu.chunk;
-      if (cu.chunk * 64 >= ntiles) {
-        tl.kb = ntiles;
-        tl.qmask = 0;
-        return;
-      }
+      if (cu.chunk * 64 >= ntiles) return Tile{ntiles, 0, 0.f, 0, 0.f, 64};
       const int kb = cu.chunk * 64 + lane;
+      TileInfo ti{64 << 8, 0.f, 0.f, 0};
+      if constexpr (SPARSE) {  // sparse passes scan many chunks per attended tile
+        ti = cu.pre;
+        if (kb + 64 < nkb) cu.pre = tinfo[kb + 64];
+      } else if (kb < nkb) {
+        ti = tinfo[kb];
+      }
       int qm = 0;
-      TileInfo ti{0, 0.f};
       if (kb < nkb) {
         if constexpr (SPARSE) {
           const int w = kb >> 5;
@@ -377,19 +403,24 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
         } else {
           qm = 1;
         }
-        if (qm) ti = tinfo[kb];
       }
       cu.mask = __ballot(qm != 0 && (is_fast(ti.flags) == want_fast));
       cu.flags_lane = ti.flags;
       cu.t_lane = ti.t;
+      cu.t2_lane = ti.t2;
       cu.qm_lane = qm;
     }
     const int bit = __builtin_ctzll(cu.mask);
     cu.mask &= cu.mask - 1;
-    tl.kb = cu.chunk * 64 + bit;
-    tl.flags = __builtin_amdgcn_readlane(cu.flags_lane, bit);
-    tl.t = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t_lane), bit));
-    tl.qmask = SPARSE ? __builtin_amdgcn_readlane(cu.qm_lane, bit) : 1;
+    const int fs = __builtin_amdgcn_readlane(cu.flags_lane, bit);
+    return Tile{
+        cu.chunk * 64 + bit,
+        fs & kTileFlagMask,
+        __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t_lane), bit)),
+        SPARSE ? __builtin_amdgcn_readlane(cu.qm_lane, bit) : 1,
+        want_fast ? 0.f
+                  : __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t2_lane), bit)),
+        fs >> 8};
   };
   // does this wave compute tile tl?
   auto attends = [&](const Tile& tl) __attribute__((always_inline)) -> bool {
@@ -505,21 +536,44 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       l_run += rs;
     } else {
       float mx = -INFINITY;
+      if (tl.flags & kTileTwoRun) {
+        // two runs, each with one per-query penalty: keys below the split take bA
+        const float bA = (PEN && q_out && (tl.flags & kTileGuideA))
+                             ? -tara_pen(fabsf(qt - tl.t), a.window, a.inv_falloff, a.strength,
+                                         a.cap) * kLog2e
+                             : 0.f;
+        const float bB = (PEN && q_out && (tl.flags & kTileGuideB))
+                             ? -tara_pen(fabsf(qt - tl.t2), a.window, a.inv_falloff, a.strength,
+                                         a.cap) * kLog2e
+                             : 0.f;
+        const int thr = tl.split - 4 * hh;  // key offset 32c + 8(r/4) + r%4 below thr: run A
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
+        for (int c = 0; c < NT; ++c) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const uint32_t sg = ksg[kl];
-          float x = sacc[c][r] * c_log2;
-          if (sg == (uint32_t)kSegInvalid) {
-            x = -INFINITY;
-          } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
-            x -= tara_pen(fabsf(qt - ktt[kl]), a.window, a.inv_falloff, a.strength, a.cap) *
-                 kLog2e;
+          for (int r = 0; r < 16; ++r) {
+            const int kofs = 32 * c + 8 * (r >> 2) + (r & 3);
+            const float x = fmaf(sacc[c][r], c_log2, kofs < thr ? bA : bB);
+            sacc[c][r] = x;
+            mx = __builtin_elementwise_maximum(mx, x);
           }
-          sacc[c][r] = x;
-          mx = __builtin_elementwise_maximum(mx, x);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kl = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const uint32_t sg = ksg[kl];
+            float x = sacc[c][r] * c_log2;
+            if (sg == (uint32_t)kSegInvalid) {
+              x = -INFINITY;
+            } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
+              x -= tara_pen(fabsf(qt - ktt[kl]), a.window, a.inv_falloff, a.strength, a.cap) *
+                   kLog2e;
+            }
+            sacc[c][r] = x;
+            mx = __builtin_elementwise_maximum(mx, x);
+          }
         }
       }
       const float tmax = pair_max_swap(mx);
@@ -538,11 +592,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   // have finished reading it, and every load has two slots to land.
   auto run_pass = [&](auto general_tag) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
-    Cursor cu{-1, 0ull, 0, 0.f, 0};
-    Tile tp{ntiles, 0, 0.f, 0}, tq{ntiles, 0, 0.f, 0}, tn{ntiles, 0, 0.f, 0};
-    cursor_next(cu, !GENERAL, tq);
+    Cursor cu = cursor_start();
+    Tile tp{ntiles, 0, 0.f, 0, 0.f, 64}, tq{ntiles, 0, 0.f, 0, 0.f, 64}, tn{ntiles, 0, 0.f, 0, 0.f, 64};
+    tq = cursor_next(cu, !GENERAL);
     if (tq.kb >= ntiles) return;
-    cursor_next(cu, !GENERAL, tn);
+    tn = cursor_next(cu, !GENERAL);
     // prologue: K_0, K_1, V_0 (and the key rows of tiles 0 and 1)
     dma_k(tq.kb, ks0);
     dma_v(tq.kb, vs0);
@@ -565,8 +619,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       // the key rows of tile j+1 were fetched during the previous softmax slot
       if (GENERAL && tn.kb < ntiles) small_store(sgnext, ttnext);
       slot_barrier<kWaitAll0>();
-      Tile tnn;
-      cursor_next(cu, !GENERAL, tnn);
+      const Tile tnn = cursor_next(cu, !GENERAL);
       if (tnn.kb < ntiles) {
         dma_k(tnn.kb, knn);
         if (GENERAL) small_load(tnn.kb);

@@ -17,10 +17,17 @@ constexpr int kBitmapWords = (kMaxBlocks + 31) / 32;
 
 // Per 64-key tile summary (see tile_info_kernel).
 constexpr int kTileAnyGuide = 1, kTileUniformGuide = 2, kTileFull = 4;
+constexpr int kTileTwoRun = 8;     // full tile of two runs of equal (segment, time)
+constexpr int kTileGuideA = 16;    // the first run is guide video
+constexpr int kTileGuideB = 32;    // the second run is guide video
 struct TileInfo {
-  int flags;
-  float t;
+  int flags;    // bits 0-7: the kTile* flags; bits 8-15: first key of the second run
+                // (two-run tiles, else 64)
+  float t;      // time of the first key
+  float t2;     // time of the second run (two-run tiles)
+  int pad;
 };
+constexpr int kTileFlagMask = 0xff;
 
 // Arguments of one attention launch (dense or block-sparse).
 struct AttnArgs {

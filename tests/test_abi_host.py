@@ -127,11 +127,11 @@ def test_workspace_sizes():
     """bf16 workspaces: a transposed v copy (keys padded to 64) and an 8-byte summary
     per 64-key tile, each 256-byte aligned; fp32 needs none."""
     L = api.lib()
-    assert L.attn_dense_tara_workspace(100, 3, 128, 1) == _a256(3 * 128 * 128 * 2) + _a256(2 * 8)
-    assert L.attn_dense_tara_workspace(128, 3, 64, 1) == _a256(3 * 64 * 128 * 2) + _a256(2 * 8)
+    assert L.attn_dense_tara_workspace(100, 3, 128, 1) == _a256(3 * 128 * 128 * 2) + _a256(2 * 16)
+    assert L.attn_dense_tara_workspace(128, 3, 64, 1) == _a256(3 * 64 * 128 * 2) + _a256(2 * 16)
     assert L.attn_dense_tara_workspace(100, 3, 128, 0) == 0
     assert L.attn_dense_tara_workspace(100, 3, 96, 1) == 0
-    assert L.attn_block_sparse_workspace(129, 2, 64, 1) == _a256(2 * 64 * 192 * 2) + _a256(3 * 8)
+    assert L.attn_block_sparse_workspace(129, 2, 64, 1) == _a256(2 * 64 * 192 * 2) + _a256(3 * 16)
     nb = (31552 + 63) // 64
     assert L.attn_block_router_workspace(31552, 24, 128, 64) >= 2 * nb * 24 * 128 * 4
     assert L.attn_block_router_workspace(31552, 24, 128, 32) == 0
@@ -202,7 +202,7 @@ def test_via_argument_checks_and_workspace():
     # non-guide runs [0, 256) and [3328, 6800), the guide run and its 12 frames of 256,
     # plus accumulator and partial buffers (o and lse) for the 3,072 output rows
     ranges = [6800, 256, 3472, 3072] + [256] * 12
-    vt = sum(_a256((r + 63) // 64 * 64 * 24 * 128 * 2) + _a256((r + 63) // 64 * 8) for r in ranges)
+    vt = sum(_a256((r + 63) // 64 * 64 * 24 * 128 * 2) + _a256((r + 63) // 64 * 16) for r in ranges)
     assert need == vt + 2 * 3072 * 24 * (128 + 1) * 4
     args = [P, P, P, 1, wl.n, 24, 128, P, P, sp, tp, 2.0, 0.2, 0.25, 6.0, 0.088, P, 1, P]
     assert L.attn_dense_tara_via(*args, None, 0, None) == -4
