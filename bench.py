@@ -316,6 +316,44 @@ def main():
                                   "ideal_speedup": 1.0 / kf}
         print("# sweep done", file=sys.stderr, flush=True)
 
+    # The isolated shape timed on the Flash Partitions page (107,126 rows x 8 heads): direct
+    # and partition-path calls, reported beside the page's figures (another GPU: context).
+    p1 = None
+    if not args.no_sweep and args.only == "all":
+        w1 = W.P1_MICRO
+        q1, k1, v1 = (dev(x) for x in W.make_qkv(w1))
+        s1, t1 = W.layout(w1)
+        s1d, t1d = torch.from_numpy(s1).cuda(), torch.from_numpy(t1).cuda()
+        o1 = torch.empty_like(q1)
+        l1 = torch.empty((w1.n, w1.heads), dtype=torch.float32, device="cuda")
+        ws1 = torch.empty(api.dense_tara_workspace_bytes(w1.n, w1.heads, w1.head_dim, 1),
+                          dtype=torch.uint8, device="cuda")
+        wv1 = torch.empty(api.via_workspace_bytes(s1, t1, w1.heads, w1.head_dim, 1),
+                          dtype=torch.uint8, device="cuda")
+        f1 = 4.0 * w1.n * w1.n * w1.head_dim * w1.heads
+        p1 = {"workload": "107,126 rows x 8 heads x d 128 bf16, TARA defaults",
+              "dense_equiv_tflop": f1 / 1e12,
+              "page_context_s": {"native_flash_attention": 0.327, "flash_partitions": 0.422,
+                                 "temporal_flex_attention": 0.628,
+                                 "hardware": "RTX PRO 6000 Blackwell (another GPU)"}}
+        for name, fn in (("direct", lambda: api.attn_dense_tara(
+                             q1, k1, v1, s1d, t1d, s1d, t1d, *w1.tara, scale=w1.scale, o=o1,
+                             lse=l1, ws=ws1)),
+                         ("via", lambda: api.attn_dense_tara_via(
+                             q1, k1, v1, s1d, t1d, s1, t1, *w1.tara, scale=w1.scale, o=o1,
+                             lse=l1, ws=wv1))):
+            ts = []
+            for rep in range(4):
+                a = ev()
+                fn()
+                b = ev()
+                torch.cuda.synchronize()
+                if rep:
+                    ts.append(a.elapsed_time(b))
+            ms1 = float(np.median(ts))
+            p1[name] = {"ms": ms1, "dense_equiv_tflops": f1 / (ms1 * 1e-3) / 1e12}
+        print("# isolated shape done", file=sys.stderr, flush=True)
+
     roofline = None
     if d:
         traffic = None
@@ -359,6 +397,7 @@ def main():
                             "cap": tara[3]}},
         "calls": calls,
         "sparsity_sweep": sweep,
+        "isolated_shape": p1,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -128,7 +128,19 @@ FULL_SPARSE = Workload(
     sparsities=(0.50, 0.70, 0.85, 0.90, 0.95), protected_prefix_len=7259,
     description="full-scale block-sparse with TARA on routed guide tiles, bf16")
 
-WORKLOADS = {w.name: w for w in (TINY_DENSE, MID_DENSE, MID_SPARSE, FULL_DENSE, FULL_SPARSE)}
+# The isolated attention shape timed on the Flash Partitions page (section 5): 107,126
+# tokens, 8 heads, d 128, bf16. The page gives no segment layout; this one keeps the
+# full-scale proportions: 5,126 text, guide 28 x 1,800, 1,200 audio, output 28 x 1,800.
+P1_MICRO = Workload(
+    name="dense_tara_107126x8_d128_bf16",
+    spans=(Span(SEG_TEXT, 5126), _video(SEG_GUIDE, 28, 1800), Span(SEG_AUDIO, 1200),
+           _video(SEG_OUTPUT, 28, 1800)),
+    heads=8, head_dim=128, dtype="bf16", seed_index=6, frame_weight=0.7,
+    protected_prefix_len=5126,
+    description="isolated dense TARA shape of the Flash Partitions page, bf16")
+
+WORKLOADS = {w.name: w for w in (TINY_DENSE, MID_DENSE, MID_SPARSE, FULL_DENSE, FULL_SPARSE,
+                                 P1_MICRO)}
 
 
 def layout(w: Workload):

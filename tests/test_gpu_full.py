@@ -105,3 +105,39 @@ def test_full_router_and_sparse_sampled(full, sparsity):
         lrf.append(lb)
     compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
             f"full sparse s={sparsity}")
+
+
+# ------------------------------------------------------------------ isolated shape
+# The isolated attention shape of the Flash Partitions page (107,126 rows x 8 heads),
+# direct and through the partition path, in the launch configuration the benchmark
+# times; sampled rows against the oracle.
+P1_HEADS = [0, 7]
+P1_BLOCKS = [0, 80, 400, 867, 880, 886, 1300, 1673]  # text/guide, guide/audio, audio/output, tail
+
+
+@pytest.fixture(scope="module")
+def micro():
+    wl = W.P1_MICRO
+    q, k, v = W.make_qkv(wl)
+    seg, t = W.layout(wl)
+    dev = dict(q=to_device(q, "bf16"), k=to_device(k, "bf16"), v=to_device(v, "bf16"),
+               seg=torch.from_numpy(seg).cuda(), t=torch.from_numpy(t).cuda())
+    host = {n: f64(x[:, P1_HEADS], "bf16") for n, x in (("q", q), ("k", k), ("v", v))}
+    return wl, seg, t, dev, host
+
+
+@pytest.mark.parametrize("path", ["direct", "via"])
+def test_p1_shape_dense_tara_sampled(micro, path):
+    wl, seg, t, dev, host = micro
+    print(f"case {wl.name} path={path}", flush=True)
+    if path == "direct":
+        o, lse = api.attn_dense_tara(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"],
+                                     dev["seg"], dev["t"], *wl.tara, scale=wl.scale)
+    else:
+        o, lse = api.attn_dense_tara_via(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], seg, t,
+                                         *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(P1_BLOCKS, wl.n)
+    o_ref, l_ref = _dense_ref(wl, seg, t, host, rows)
+    ri = torch.from_numpy(rows).cuda()
+    compare(o[ri][:, P1_HEADS], lse[ri][:, P1_HEADS], o_ref, l_ref, "bf16", f"p1 shape {path}")
