@@ -23,10 +23,11 @@ from .tara import (tara_penalty, tara_bias, dense_tara, plain_attention, lse_mer
                    tara_partitions, runs)
 from .router import (router_plan, select_count, block_means_fp32, pooled_scores_fp32,
                      select_topk, route_head)
-from .sparse import block_sparse_block, block_sparse
+from .sparse import block_sparse_block, block_sparse, tail_terms
 
 __all__ = [
     "tara_penalty", "tara_bias", "dense_tara", "plain_attention", "lse_merge",
     "tara_partitions", "runs", "router_plan", "select_count", "block_means_fp32",
     "pooled_scores_fp32", "select_topk", "route_head", "block_sparse_block", "block_sparse",
+    "tail_terms",
 ]

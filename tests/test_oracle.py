@@ -537,3 +537,92 @@ def test_pins_catch_planted_router_mistakes(monkeypatch):
 
     assert not np.array_equal(reversed_ties(sc, video, 5), _brute_topk(sc, video, 5))
     assert np.array_equal(good(sc, video, 5), _brute_topk(sc, video, 5))
+
+
+# ------------------------------------------------------------------ tail term
+def _constant_block_case(n=16 + 7 * 16 + 9, bs=16, d=8, seed=7):
+    """q, k, v whose rows are identical within every block (ragged last block of 9 rows):
+    then each block's pooled centroids equal its rows exactly."""
+    rng = np.random.default_rng(seed)
+    nb = (n + bs - 1) // bs
+    seg = np.full(n, W.SEG_GUIDE, dtype=np.uint8)
+    seg[:16] = W.SEG_TEXT
+    t = np.zeros(n, dtype=np.float32)
+    def rows(scale):
+        blocks = (rng.standard_normal((nb, d)) * scale).astype(np.float32)
+        return np.repeat(blocks, bs, axis=0)[:n]
+    return seg, t, rows(1.0), rows(1.0), rows(1.0), nb
+
+
+def test_tail_term_is_exact_for_constant_blocks():
+    """With identical rows inside every block, the pooled tail term stands in exactly for
+    the left-out tiles, so sparse + tail reproduces dense attention over every key (the
+    only difference is the float32 rounding of the pooled score)."""
+    seg, t, q32, k32, v32, nb = _constant_block_case()
+    bs, scale, params = 16, 0.35, (0.0, 0.2, 0.25, 6.0)
+    _, prot, video, _ = oracle.router_plan(seg, 16, bs, 0.0)
+    k_sel = 2
+    tiles = oracle.route_head(q32, k32, seg, 16, bs, k_sel)
+    q, k, v = (x.astype(np.float64) for x in (q32, k32, v32))
+    L, vt = oracle.tail_terms(q32, k32, v, seg, 16, bs, tiles, scale)
+    assert np.all(np.isfinite(L))
+    o_d, l_d = oracle.dense_tara(q[:, None], k[:, None], v[:, None], seg, t, seg, t, params, scale)
+    for qb in range(nb):
+        ob, lb = oracle.block_sparse_block(q, k, v, seg, t, params, scale, bs, prot, tiles[qb], qb,
+                                           tail=(L[qb], vt[qb]))
+        lo, hi = qb * bs, min(len(seg), qb * bs + bs)
+        assert np.max(np.abs(ob - o_d[lo:hi, 0])) < 1e-5
+        assert np.max(np.abs(lb - l_d[lo:hi, 0])) < 1e-5
+    # without the tail the same call drops the left-out mass
+    ob, lb = oracle.block_sparse_block(q, k, v, seg, t, params, scale, bs, prot, tiles[3], 3)
+    assert np.max(np.abs(lb - l_d[48:64, 0])) > 1e-3
+
+
+def test_tail_term_vanishes_without_left_out_tiles():
+    """Every video tile routed (sparsity 0): no tail term, sparse output unchanged."""
+    wl, seg, t, q, k, v = _sparse_case()
+    nb, prot, vid, kk = oracle.router_plan(seg, 40, 16, 0.0)
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    tiles = oracle.route_head(q[:, 0], k[:, 0], seg, 40, 16, kk)
+    L, vt = oracle.tail_terms(q[:, 0], k[:, 0], v64[:, 0], seg, 40, 16, tiles, wl.scale)
+    assert np.all(np.isneginf(L)) and np.all(vt == 0.0)
+    for qb in (0, 3):
+        a = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t, wl.tara, wl.scale,
+                                      16, prot, tiles[qb], qb, tail=(L[qb], vt[qb]))
+        b = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t, wl.tara, wl.scale,
+                                      16, prot, tiles[qb], qb)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_tail_pin_catches_planted_mistakes():
+    """The constant-block pin fails for a tail without the row counts or without the
+    value weighting (mistakes planted in a copy of the oracle's reduction)."""
+    seg, t, q32, k32, v32, nb = _constant_block_case()
+    bs, scale, params = 16, 0.35, (0.0, 0.2, 0.25, 6.0)
+    _, prot, video, _ = oracle.router_plan(seg, 16, bs, 0.0)
+    tiles = oracle.route_head(q32, k32, seg, 16, bs, 2)
+    q, k, v = (x.astype(np.float64) for x in (q32, k32, v32))
+    o_d, _ = oracle.dense_tara(q[:, None], k[:, None], v[:, None], seg, t, seg, t, params, scale)
+    qbar = oracle.block_means_fp32(q32, bs)
+    kbar = oracle.block_means_fp32(k32, bs)
+    vbar = np.stack([v[b * bs:min(len(v), b * bs + bs)].mean(axis=0) for b in range(nb)])
+    S = oracle.pooled_scores_fp32(qbar, kbar[video]).astype(np.float64)
+    counts = np.array([min(len(v), b * bs + bs) - b * bs for b in video], dtype=np.float64)
+
+    def worst(use_counts, weight_values):
+        err = 0.0
+        for qb in range(nb):
+            keep = np.array([b not in set(tiles[qb].tolist()) for b in video])
+            x = scale * S[qb, keep] + (np.log(counts[keep]) if use_counts else 0.0)
+            w = np.exp(x - x.max())
+            L = x.max() + np.log(w.sum())
+            vt = ((w[:, None] * vbar[video[keep]]).sum(0) / w.sum() if weight_values
+                  else vbar[video[keep]].mean(0))
+            ob, _ = oracle.block_sparse_block(q, k, v, seg, t, params, scale, bs, prot, tiles[qb],
+                                              qb, tail=(L, vt))
+            lo, hi = qb * bs, min(len(seg), qb * bs + bs)
+            err = max(err, float(np.max(np.abs(ob - o_d[lo:hi, 0]))))
+        return err
+    assert worst(True, True) < 1e-5
+    assert worst(False, True) > 1e-3
+    assert worst(True, False) > 1e-3
