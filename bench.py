@@ -354,6 +354,35 @@ def main():
             p1[name] = {"ms": ms1, "dense_equiv_tflops": f1 / (ms1 * 1e-3) / 1e12}
         print("# isolated shape done", file=sys.stderr, flush=True)
 
+    # NEXT row: the pooled tail term at the benchmark sparsity (router with tail + sparse with
+    # tail), outside the step value
+    next_rows = None
+    if not args.no_sweep and args.only == "all":
+        tl_lse = torch.empty((H, nb), dtype=torch.float32, device="cuda")
+        tl_v = torch.empty((H, nb, D), dtype=torch.float32, device="cuda")
+        ws_rt = torch.empty(api.router_tail_workspace_bytes(N, H, D), dtype=torch.uint8,
+                            device="cuda")
+        rt, st = [], []
+        for rep in range(4):
+            a = ev()
+            api.attn_block_router_tail(qd, kd, vd, segd, wl.protected_prefix_len, k_sel, n_prot,
+                                       scale=scale, tiles=tiles, prot=prot, tail_lse=tl_lse,
+                                       tail_v=tl_v, ws=ws_rt)
+            b = ev()
+            api.attn_block_sparse_tail(qd, kd, vd, segd, td, tiles, prot, tl_lse, tl_v, *tara,
+                                       scale=scale, o=o_sparse, lse=l_sparse, ws=ws_dense)
+            c = ev()
+            torch.cuda.synchronize()
+            if rep:
+                rt.append(a.elapsed_time(b))
+                st.append(b.elapsed_time(c))
+        tot = float(np.median(rt) + np.median(st))
+        next_rows = {"tail_correction": {
+            "sparsity": args.sparsity, "router_tail_ms": float(np.median(rt)),
+            "sparse_tail_ms": float(np.median(st)), "ms": tot,
+            "speedup_vs_dense": (d["ms"] / tot) if d else None}}
+        print("# tail term done", file=sys.stderr, flush=True)
+
     roofline = None
     if d:
         traffic = None
@@ -398,6 +427,7 @@ def main():
         "calls": calls,
         "sparsity_sweep": sweep,
         "isolated_shape": p1,
+        "next_rows": next_rows,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -25,6 +25,7 @@ EXPORTS = (
     "attn_dense_tara_workspace", "attn_dense_tara",
     "attn_router_plan", "attn_block_router_workspace", "attn_block_router",
     "attn_block_sparse_workspace", "attn_block_sparse",
+    "attn_block_router_tail_workspace", "attn_block_router_tail", "attn_block_sparse_tail",
     "partition_lse_merge",
     "attn_dense_tara_via_workspace", "attn_dense_tara_via",
 )
@@ -43,6 +44,12 @@ _SIGS = {
     "attn_block_sparse_workspace": (_sz, [_i, _i, _i, _i]),
     "attn_block_sparse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f, _f,
                                _i, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _sz, _vp]),
+    "attn_block_router_tail_workspace": (_sz, [_i, _i, _i, _i]),
+    "attn_block_router_tail": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _f, _vp,
+                                    _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "attn_block_sparse_tail": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f,
+                                    _f, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _sz,
+                                    _vp]),
     "partition_lse_merge": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _vp]),
     "attn_dense_tara_via_workspace": (_sz, [_vp, _vp, _i, _i, _i, _i]),
     "attn_dense_tara_via": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -196,6 +203,41 @@ def attn_block_router(q, k, seg, protected_prefix_len, k_sel, n_prot, block_size
     return tiles, prot
 
 
+def router_tail_workspace_bytes(n, heads, head_dim, block_size=64):
+    return int(lib().attn_block_router_tail_workspace(n, heads, head_dim, block_size))
+
+
+def attn_block_router_tail(q, k, v, seg, protected_prefix_len, k_sel, n_prot, scale=None,
+                           block_size=64, tiles=None, prot=None, tail_lse=None, tail_v=None,
+                           ws=None, stream=None):
+    """Pooled router with the tail term: returns (tiles, prot, tail_lse [H, nb],
+    tail_v [H, nb, D])."""
+    import torch
+    n, H, D = q.shape
+    nb = (n + block_size - 1) // block_size
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if tiles is None:
+        tiles = torch.empty((H, nb, k_sel), dtype=torch.int32, device=q.device)
+    if prot is None:
+        prot = torch.empty((n_prot,), dtype=torch.int32, device=q.device)
+    if tail_lse is None:
+        tail_lse = torch.empty((H, nb), dtype=torch.float32, device=q.device)
+    if tail_v is None:
+        tail_v = torch.empty((H, nb, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(router_tail_workspace_bytes(n, H, D, block_size), q.device)
+    _contig(q, k, v, seg, tiles, prot, tail_lse, tail_v)
+    st = lib().attn_block_router_tail(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), n, H, D,
+                                      _ptr(seg), protected_prefix_len, block_size, k_sel, scale,
+                                      _ptr(tiles) if k_sel > 0 else None,
+                                      _ptr(prot) if n_prot > 0 else None, n_prot,
+                                      _ptr(tail_lse), _ptr(tail_v), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_block_router_tail", st)
+    return tiles, prot, tail_lse, tail_v
+
+
 def attn_block_sparse(q, k, v, seg, t, tiles, prot, strength=2.0, window=0.20, falloff=0.25,
                       cap=6.0, scale=None, block_size=64, o=None, o_dtype=None, lse=None,
                       ws=None, stream=None):
@@ -221,6 +263,35 @@ def attn_block_sparse(q, k, v, seg, t, tiles, prot, strength=2.0, window=0.20, f
                                  _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(stream))
     _check("attn_block_sparse", st)
+    return o, lse
+
+
+def attn_block_sparse_tail(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, strength=2.0,
+                           window=0.20, falloff=0.25, cap=6.0, scale=None, block_size=64, o=None,
+                           o_dtype=None, lse=None, ws=None, stream=None):
+    """Block-sparse attention with the pooled tail key per query block: returns (o, lse)."""
+    import torch
+    n, H, D = q.shape
+    dt = _dtype_code(q)
+    k_sel = int(tiles.shape[-1]) if tiles is not None else 0
+    n_prot = int(prot.numel()) if prot is not None else 0
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if ws is None:
+        ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
+    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    st = lib().attn_block_sparse_tail(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
+                                      strength, window, falloff, cap, scale, block_size,
+                                      _ptr(tiles) if k_sel > 0 else None, k_sel,
+                                      _ptr(prot) if n_prot > 0 else None, n_prot,
+                                      _ptr(tail_lse), _ptr(tail_v), _ptr(o), _dtype_code(o),
+                                      _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(stream))
+    _check("attn_block_sparse_tail", st)
     return o, lse
 
 

@@ -52,6 +52,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, 
   a.scale = scale;
   a.strength = strength; a.window = window; a.inv_falloff = 1.f / falloff; a.cap = cap;
   a.prot = nullptr; a.n_prot = 0; a.tiles = nullptr; a.k_sel = 0; a.nqb = 0;
+  a.tail_lse = nullptr; a.tail_v = nullptr;
   return a;
 }
 
@@ -251,14 +252,25 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
 
 size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size) {
   if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || block_size != kTile) return 0;
-  return router_ws_bytes(n, heads, head_dim);
+  return router_ws_bytes(n, heads, head_dim, false);
 }
 
-int attn_block_router(const void* q, const void* k, int dtype, int n, int heads, int head_dim,
-                      const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
-                      int32_t* tiles, int32_t* prot, int n_prot, void* ws, size_t ws_bytes,
-                      void* stream) {
+size_t attn_block_router_tail_workspace(int n, int heads, int head_dim, int block_size) {
+  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || block_size != kTile) return 0;
+  return router_ws_bytes(n, heads, head_dim, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+int route(const void* q, const void* k, const void* v, int dtype, int n, int heads,
+          int head_dim, const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
+          int32_t* tiles, int32_t* prot, int n_prot, bool tail, float scale, float* tail_lse,
+          float* tail_v, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !seg || n <= 0 || heads <= 0) return H3_EINVAL;
+  if (tail && (!v || !tail_lse || !tail_v || !std::isfinite(scale) || !(scale > 0.f)))
+    return H3_EINVAL;
   if (protected_prefix_len < 0 || protected_prefix_len > n) return H3_EINVAL;
   if (k_sel < 0 || n_prot < 0 || (k_sel > 0 && !tiles) || (n_prot > 0 && !prot))
     return H3_EINVAL;
@@ -267,13 +279,66 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
   const int nb = (n + kTile - 1) / kTile;
   if (k_sel > nb) return H3_EINVAL;
   if (nb > router_max_blocks()) return H3_EUNSUPPORTED;
-  const size_t need = router_ws_bytes(n, heads, head_dim);
+  const size_t need = router_ws_bytes(n, heads, head_dim, tail);
   if (!ws || ws_bytes < need) return H3_EWORKSPACE;
-  RouterWs w = router_ws_carve(ws, n, heads, head_dim);
-  hipError_t e = launch_router(q, k, dtype == H3_DTYPE_BF16, n, heads, head_dim, seg,
-                               protected_prefix_len, k_sel, tiles, prot, n_prot, w,
+  RouterWs w = router_ws_carve(ws, n, heads, head_dim, tail);
+  hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, seg,
+                               protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
+                               tail ? tail_lse : nullptr, tail ? tail_v : nullptr,
                                (hipStream_t)stream);
   return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+int sparse(const void* q, const void* k, const void* v, int dtype, int n, int heads,
+           int head_dim, const uint8_t* seg, const float* t, float strength, float window,
+           float falloff, float cap, float scale, int block_size, const int32_t* tiles,
+           int k_sel, const int32_t* prot, int n_prot, const float* tail_lse,
+           const float* tail_v, void* o, int o_dtype, float* lse, void* ws, size_t ws_bytes,
+           void* stream) {
+  if (!q || !k || !v || !seg || !t || !o || !lse) return H3_EINVAL;
+  if (n <= 0 || heads <= 0) return H3_EINVAL;
+  if (k_sel < 0 || n_prot < 0 || k_sel + n_prot == 0) return H3_EINVAL;
+  if ((k_sel > 0 && !tiles) || (n_prot > 0 && !prot)) return H3_EINVAL;
+  if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || block_size != kTile ||
+      heads > 65535)
+    return H3_EUNSUPPORTED;
+  if ((n + kTile - 1) / kTile > kMaxBlocks) return H3_EUNSUPPORTED;
+  const size_t need = attn_dense_tara_workspace(n, heads, head_dim, dtype);
+  if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
+  AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
+                         scale, o, o_dtype, lse);
+  a.prot = prot;
+  a.n_prot = n_prot;
+  a.tiles = tiles;
+  a.k_sel = k_sel;
+  a.nqb = (n + kTile - 1) / kTile;
+  a.tail_lse = tail_lse;
+  a.tail_v = tail_v;
+  const bool pen = strength > 0.f && cap > 0.f;
+  hipError_t e = run_attention(a, dtype, head_dim, true, pen, ws, false, (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_block_router(const void* q, const void* k, int dtype, int n, int heads, int head_dim,
+                      const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
+                      int32_t* tiles, int32_t* prot, int n_prot, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return route(q, k, nullptr, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size,
+               k_sel, tiles, prot, n_prot, false, 0.f, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int attn_block_router_tail(const void* q, const void* k, const void* v, int dtype, int n,
+                           int heads, int head_dim, const uint8_t* seg, int protected_prefix_len,
+                           int block_size, int k_sel, float scale, int32_t* tiles, int32_t* prot,
+                           int n_prot, float* tail_lse, float* tail_v, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return route(q, k, v, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size, k_sel,
+               tiles, prot, n_prot, true, scale, tail_lse, tail_v, ws, ws_bytes, stream);
 }
 
 size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype) {
@@ -285,27 +350,21 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, in
                       float window, float falloff, float cap, float scale, int block_size,
                       const int32_t* tiles, int k_sel, const int32_t* prot, int n_prot, void* o,
                       int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (!q || !k || !v || !seg || !t || !o || !lse) return H3_EINVAL;
-  if (n <= 0 || heads <= 0) return H3_EINVAL;
-  if (k_sel < 0 || n_prot < 0 || k_sel + n_prot == 0) return H3_EINVAL;
-  if ((k_sel > 0 && !tiles) || (n_prot > 0 && !prot)) return H3_EINVAL;
-  if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
-  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || block_size != kTile ||
-      heads > 65535)
-    return H3_EUNSUPPORTED;
-  if ((n + kTile - 1) / kTile > kMaxBlocks) return H3_EUNSUPPORTED;
-  const size_t need = attn_block_sparse_workspace(n, heads, head_dim, dtype);
-  if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
-  AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
-                         scale, o, o_dtype, lse);
-  a.prot = prot;
-  a.n_prot = n_prot;
-  a.tiles = tiles;
-  a.k_sel = k_sel;
-  a.nqb = (n + kTile - 1) / kTile;
-  const bool pen = strength > 0.f && cap > 0.f;
-  hipError_t e = run_attention(a, dtype, head_dim, true, pen, ws, false, (hipStream_t)stream);
-  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
+  return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
+                scale, block_size, tiles, k_sel, prot, n_prot, nullptr, nullptr, o, o_dtype, lse,
+                ws, ws_bytes, stream);
+}
+
+int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtype, int n,
+                           int heads, int head_dim, const uint8_t* seg, const float* t,
+                           float strength, float window, float falloff, float cap, float scale,
+                           int block_size, const int32_t* tiles, int k_sel, const int32_t* prot,
+                           int n_prot, const float* tail_lse, const float* tail_v, void* o,
+                           int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!tail_lse || !tail_v) return H3_EINVAL;
+  return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
+                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v, o, o_dtype, lse,
+                ws, ws_bytes, stream);
 }
 
 int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

@@ -645,7 +645,27 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   run_pass(std::true_type{});
 
   // ---- combine lane halves, then normalise
-  const float l_tot = pair_sum_swap(l_run);
+  float l_tot = pair_sum_swap(l_run);
+  // optional tail key of the query block: one more softmax term with logit tail_lse and
+  // value tail_v, merged like any other key (log2 units here)
+  float tail_w = 0.f;
+  const float* tail_v = nullptr;
+  if (SPARSE && a.tail_lse && qvalid) {
+    const int64_t tb = (int64_t)h * a.nqb + qrow / kTile;
+    const float lt = a.tail_lse[tb] * kLog2e;
+    if (lt != -INFINITY) {
+      const float m_new = __builtin_elementwise_maximum(m_run, lt);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      tail_w = __builtin_amdgcn_exp2f(lt - m_new);
+      l_tot = l_tot * alpha + tail_w;
+      m_run = m_new;
+      tail_v = a.tail_v + tb * D;
+    }
+  }
   if (qvalid) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t obase = ((int64_t)qrow * H + h) * D;
@@ -654,9 +674,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 ov;
+        const int d = 32 * dt + 8 * g + 4 * hh;
+        if (tail_v) {
+          const f32x4 tv = *(const f32x4*)(tail_v + d);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oacc[dt][4 * g + j] += tail_w * tv[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) ov[j] = oacc[dt][4 * g + j] * inv;
-        const int d = 32 * dt + 8 * g + 4 * hh;
         if (a.o_f32) {
           *(f32x4*)((float*)a.o + obase + d) = ov;
         } else {

@@ -121,11 +121,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     }
   }
   if (!qvalid) return;
+  // optional tail key of the query block: one more softmax term with logit tail_lse
+  // and value tail_v
+  float tail_w = 0.f;
+  const float* tail_v = nullptr;
+  if (SPARSE && a.tail_lse) {
+    const int64_t tb = (int64_t)h * a.nqb + qblk;
+    const float lt = a.tail_lse[tb];
+    if (lt != -INFINITY) {
+      const float m_new = fmaxf(m, lt);
+      const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] *= alpha;
+      tail_w = expf(lt - m_new);
+      l = l * alpha + tail_w;
+      m = m_new;
+      tail_v = a.tail_v + tb * D;
+    }
+  }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t ob = ((int64_t)qrow * H + h) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const float val = o[d] * inv;
+    const float val = (tail_v ? o[d] + tail_w * tail_v[d] : o[d]) * inv;
     if (a.o_f32)
       ((float*)a.o)[ob + d] = val;
     else

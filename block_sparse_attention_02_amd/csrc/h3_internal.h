@@ -52,6 +52,9 @@ struct AttnArgs {
   const int32_t* tiles;     // [H][nqb][k_sel]
   int k_sel;
   int nqb;
+  // optional tail key per query block (block-sparse with tail term), else null
+  const float* tail_lse;    // [H][nqb] natural log
+  const float* tail_v;      // [H][nqb][D]
 };
 
 // Rounds a key count up to whole 64-key tiles.
@@ -72,13 +75,23 @@ struct RouterWs {
   float* kbar;     // [H][D][nb] (d-major)
   int32_t* video;  // [nb]
   int32_t* counts; // [2]: n_prot, n_video
+  float* vbar;     // [H][nb][D] (tail term only, else null)
 };
-size_t router_ws_bytes(int n, int H, int D);
-RouterWs router_ws_carve(void* ws, int n, int H, int D);
+// Tail term of the unrouted tiles (see router.hip); all pointers null when not wanted.
+struct TailArgs {
+  float scale;         // attention scale applied to the pooled scores
+  int n;               // rows of the sequence (counts of the ragged last tile)
+  const float* vbar;   // [H][nb][D] block means of v
+  float* lse;          // [H][nb] natural-log logit of the tail key
+  float* v;            // [H][nb][D] value of the tail key
+};
+size_t router_ws_bytes(int n, int H, int D, bool tail);
+RouterWs router_ws_carve(void* ws, int n, int H, int D, bool tail);
 int router_max_blocks();
-hipError_t launch_router(const void* q, const void* k, bool bf16, int n, int H, int D,
-                         const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
-                         int32_t* prot, int prot_cap, const RouterWs& w, hipStream_t s);
+hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
+                         int D, const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
+                         int32_t* prot, int prot_cap, const RouterWs& w, float scale,
+                         float* tail_lse, float* tail_v, hipStream_t s);
 
 // LSE merge and accumulator finalisation.
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

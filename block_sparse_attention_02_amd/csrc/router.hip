@@ -14,6 +14,10 @@
 //                video tile in LDS (float32 products added in order of d, no fused
 //                multiply-add), then an exact radix select of the k best per query block
 //                with ties to the lower tile index, emitted in ascending tile order.
+// With the tail term ("H3 SLA Attention", inputs table, tail_correction) the pool pass
+// also takes the mean of V, and the top-k kernel folds the unrouted video tiles of each
+// query block into one pooled key: logit ln sum_u n_u exp(scale * S[qb,u]) and value the
+// same-weighted mean of their V means, from the same float32 pooled scores.
 #include "h3_internal.h"
 
 #pragma clang fp contract(off)
@@ -80,49 +84,63 @@ __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __res
 
 // ------------------------------------------------------------------ 2. pool
 // Thread = 8 consecutive (head, d) elements of a row; workgroup = one 64-row block.
-template <bool BF16, int D>
+template <bool BF16, int D, bool TAIL>
 __global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict__ q,
-                                                          const void* __restrict__ k, int n,
+                                                          const void* __restrict__ k,
+                                                          const void* __restrict__ v, int n,
                                                           int H, int nb,
                                                           float* __restrict__ qbar,
-                                                          float* __restrict__ kbar) {
+                                                          float* __restrict__ kbar,
+                                                          float* __restrict__ vbar) {
   const int b = blockIdx.x;
   const int e0 = (blockIdx.y * 128 + threadIdx.x) * 8;
   if (e0 >= H * D) return;
   const int h = e0 / D, d0 = e0 % D;
   const int lo = b * kTile, hi = min(n, lo + kTile);
   const int64_t rs = (int64_t)H * D;
-  float aq[8], ak[8];
+  float aq[8], ak[8], av[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { aq[i] = 0.f; ak[i] = 0.f; }
+  for (int i = 0; i < 8; ++i) { aq[i] = 0.f; ak[i] = 0.f; av[i] = 0.f; }
 #pragma unroll 8
   for (int r = lo; r < hi; ++r) {
     const int64_t off = (int64_t)r * rs + e0;
-    float xq[8], xk[8];
+    float xq[8], xk[8], xv[8];
     if (BF16) {
       const u32x4 uq = *(const u32x4*)((const uint16_t*)q + off);
       const u32x4 uk = *(const u32x4*)((const uint16_t*)k + off);
+      u32x4 uv = {0u, 0u, 0u, 0u};
+      if (TAIL) uv = *(const u32x4*)((const uint16_t*)v + off);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xq[2 * i] = __uint_as_float(uq[i] << 16);
         xq[2 * i + 1] = __uint_as_float(uq[i] & 0xFFFF0000u);
         xk[2 * i] = __uint_as_float(uk[i] << 16);
         xk[2 * i + 1] = __uint_as_float(uk[i] & 0xFFFF0000u);
+        xv[2 * i] = __uint_as_float(uv[i] << 16);
+        xv[2 * i + 1] = __uint_as_float(uv[i] & 0xFFFF0000u);
       }
     } else {
       const f32x4* pq = (const f32x4*)((const float*)q + off);
       const f32x4* pk = (const f32x4*)((const float*)k + off);
       const f32x4 q0 = pq[0], q1 = pq[1], k0 = pk[0], k1 = pk[1];
+      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+      if (TAIL) {
+        const f32x4* pv = (const f32x4*)((const float*)v + off);
+        v0 = pv[0];
+        v1 = pv[1];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xq[i] = q0[i]; xq[4 + i] = q1[i];
         xk[i] = k0[i]; xk[4 + i] = k1[i];
+        xv[i] = v0[i]; xv[4 + i] = v1[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       aq[i] = __fadd_rn(aq[i], xq[i]);
       ak[i] = __fadd_rn(ak[i], xk[i]);
+      if (TAIL) av[i] = __fadd_rn(av[i], xv[i]);
     }
   }
   const float cnt = (float)(hi - lo);
@@ -132,6 +150,11 @@ __global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict
   for (int i = 0; i < 8; ++i) {
     oq[i] = __fdiv_rn(aq[i], cnt);
     ok[(int64_t)i * nb] = __fdiv_rn(ak[i], cnt);
+  }
+  if (TAIL) {
+    float* ov = vbar + ((int64_t)h * nb + b) * D + d0;  // [H][nb][D]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = __fdiv_rn(av[i], cnt);
   }
 }
 
@@ -154,13 +177,14 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D, int QB>
+template <int D, int QB, bool TAIL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar,
                                                           const int32_t* __restrict__ video,
                                                           const int32_t* __restrict__ counts,
                                                           int nb, int k_sel,
-                                                          int32_t* __restrict__ tiles) {
+                                                          int32_t* __restrict__ tiles,
+                                                          TailArgs tail) {
   static_assert(QB == 1 || QB == 4, "query blocks per workgroup");
   extern __shared__ float sc[];  // [QB][nv] pooled scores
   __shared__ __attribute__((aligned(16))) float qs[D][QB];  // qbar, d-major
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 
   const int qb = qb0 + w;
-  if (!active || qb >= nb || k_sel == 0) return;
+  if (active && qb < nb && k_sel > 0) {
   int32_t* out = tiles + ((int64_t)h * nb + qb) * k_sel;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int pos = 0, eq_seen = 0;
@@ -272,67 +296,139 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     const int eq_rank = eq_seen + __popcll(eqm & below);
     const bool sel = gt || (eq && eq_rank < rem);
     const uint64_t selm = __ballot(sel);
-    if (sel) out[pos + __popcll(selm & below)] = video[i];
+    if (sel) {
+      out[pos + __popcll(selm & below)] = video[i];
+      if (TAIL) sc[w * nv + i] = -INFINITY;  // routed: not part of the tail
+    }
     pos += __popcll(selm);
     eq_seen += __popcll(eqm);
   }
   for (int j = kk + lane; j < k_sel; j += 64) out[j] = -1;
+  }
+  if (!TAIL) return;
+
+  // ---- tail term of each query block from the unrouted video tiles: weights in place
+  // of the scores, logit to tail.lse, then the weighted V means to tail.v
+  __shared__ float tsum[QB];
+  if (active) {
+    float* my_w = sc + w * nv;
+    float mx = -INFINITY;
+    for (int i = lane; i < nv; i += 64) {
+      const float s = my_w[i];
+      if (s != -INFINITY) {
+        const int kb = video[i];
+        const float x = s * tail.scale + __logf((float)min(kTile, tail.n - kb * kTile));
+        my_w[i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float sum = 0.f;
+    for (int i = lane; i < nv; i += 64) {
+      const float x = my_w[i];
+      const float e = (x == -INFINITY) ? 0.f : __expf(x - mx);
+      my_w[i] = e;
+      sum += e;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) {
+      tsum[w] = sum;
+      if (qb < nb) tail.lse[(int64_t)h * nb + qb] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
+    }
+  }
+  __syncthreads();
+  constexpr int GROUPS = 256 / D;  // query blocks handled side by side
+  const int d = tid % D, g = tid / D;
+  for (int j0 = g; j0 < QB; j0 += GROUPS) {
+    float acc = 0.f;
+    const float* wj = sc + j0 * nv;
+    for (int i = 0; i < nv; ++i) {
+      const float wt = wj[i];
+      if (wt != 0.f) acc += wt * tail.vbar[((int64_t)h * nb + video[i]) * D + d];
+    }
+    const int qj = qb0 + j0;
+    if (qj < nb) {
+      const float sm = tsum[j0];
+      tail.v[((int64_t)h * nb + qj) * D + d] = sm > 0.f ? acc / sm : 0.f;
+    }
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t router_ws_bytes(int n, int H, int D) {
+size_t router_ws_bytes(int n, int H, int D, bool tail) {
   const size_t nb = (size_t)((n + kTile - 1) / kTile);
-  return 2 * align256(nb * H * D * sizeof(float)) + align256(nb * sizeof(int32_t)) + 256;
+  const size_t means = align256(nb * H * D * sizeof(float));
+  return (tail ? 3 : 2) * means + align256(nb * sizeof(int32_t)) + 256;
 }
 
-RouterWs router_ws_carve(void* ws, int n, int H, int D) {
+RouterWs router_ws_carve(void* ws, int n, int H, int D, bool tail) {
   const size_t nb = (size_t)((n + kTile - 1) / kTile);
+  const size_t means = align256(nb * H * D * sizeof(float));
   char* p = (char*)ws;
   RouterWs w;
   w.qbar = (float*)p;
-  p += align256(nb * H * D * sizeof(float));
+  p += means;
   w.kbar = (float*)p;
-  p += align256(nb * H * D * sizeof(float));
+  p += means;
   w.video = (int32_t*)p;
   p += align256(nb * sizeof(int32_t));
   w.counts = (int32_t*)p;
+  p += 256;
+  w.vbar = tail ? (float*)p : nullptr;
   return w;
 }
 
 // Largest block count the score/top-k kernel keeps in LDS (QB x nb floats).
 int router_max_blocks() { return kMaxBlocks; }
 
-hipError_t launch_router(const void* q, const void* k, bool bf16, int n, int H, int D,
-                         const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
-                         int32_t* prot, int prot_cap, const RouterWs& w, hipStream_t s) {
-  const int nb = (n + kTile - 1) / kTile;
-  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, prot, prot_cap, w.video, w.counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+template <int D, int QB, bool TAIL>
+void launch_topk(dim3 grid, size_t lds, hipStream_t s, const RouterWs& w, int nb, int k_sel,
+                 int32_t* tiles, const TailArgs& ta) {
+  router_topk_kernel<D, QB, TAIL><<<grid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb,
+                                                         k_sel, tiles, ta);
+}
+
+template <int D, bool TAIL>
+void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, int n, int H,
+                      int nb, int k_sel, int32_t* tiles, const RouterWs& w, const TailArgs& ta,
+                      hipStream_t s) {
   const int chunks = (H * D / 8 + 127) / 128;
   dim3 pgrid(nb, chunks);
-  if (bf16) {
-    if (D == 128) router_pool_kernel<true, 128><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
-    else router_pool_kernel<true, 64><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
-  } else {
-    if (D == 128) router_pool_kernel<false, 128><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
-    else router_pool_kernel<false, 64><<<pgrid, 128, 0, s>>>(q, k, n, H, nb, w.qbar, w.kbar);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (bf16)
+    router_pool_kernel<true, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, w.qbar, w.kbar, w.vbar);
+  else
+    router_pool_kernel<false, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, w.qbar, w.kbar, w.vbar);
   const bool wide = (size_t)4 * nb * sizeof(float) <= 56 * 1024;
   const int qb = wide ? 4 : 1;
   dim3 tgrid((nb + qb - 1) / qb, H);
   const size_t lds = (size_t)qb * nb * sizeof(float);
-  if (wide) {
-    if (D == 128) router_topk_kernel<128, 4><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
-    else router_topk_kernel<64, 4><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+  if (wide)
+    launch_topk<D, 4, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
+  else
+    launch_topk<D, 1, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
+}
+
+hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
+                         int D, const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
+                         int32_t* prot, int prot_cap, const RouterWs& w, float scale,
+                         float* tail_lse, float* tail_v, hipStream_t s) {
+  const int nb = (n + kTile - 1) / kTile;
+  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, prot, prot_cap, w.video, w.counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool tail = tail_lse != nullptr;
+  const TailArgs ta{scale, n, w.vbar, tail_lse, tail_v};
+  if (D == 128) {
+    if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
+    else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
   } else {
-    if (D == 128) router_topk_kernel<128, 1><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
-    else router_topk_kernel<64, 1><<<tgrid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb, k_sel, tiles);
+    if (tail) launch_pool_topk<64, true>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
+    else launch_pool_topk<64, false>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
   }
   return hipGetLastError();
 }

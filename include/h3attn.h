@@ -159,6 +159,51 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Routing with the pooled tail term.
+ * From "H3 SLA Attention", inputs table (tail_correction): instead of a hard
+ * zero for the video tiles the top-k leaves out, one pooled term stands in for
+ * all of them, scored from the pooled centroids the selection already computes.
+ * Reading (the page gives no formula): for query block qb of head h and its
+ * unrouted video tiles U,
+ *   tail_lse[h][qb] = ln sum_{u in U} n_u * exp(scale * S[qb][u]),
+ *   tail_v[h][qb][:] = sum_u n_u exp(scale * S[qb][u]) vbar_u / exp(tail_lse),
+ * with S the float32 pooled score used for routing, n_u the rows of tile u and
+ * vbar_u the float32 mean of its v rows; (-inf, 0) when U is empty.
+ * Same routing outputs and rules as attn_block_router, plus:
+ * v:        device [n][heads][head_dim] values (dtype as q/k);
+ * scale:    the attention scale of the sparse call (> 0);
+ * tail_lse: device float32 [heads][ceil(n/64)]; tail_v: device float32
+ *           [heads][ceil(n/64)][head_dim].
+ * Workspace: attn_block_router_tail_workspace(n, heads, head_dim, block_size).
+ * Errors: as attn_block_router, plus H3_EINVAL for null v/tail_lse/tail_v or a
+ * non-finite or non-positive scale.
+ */
+size_t attn_block_router_tail_workspace(int n, int heads, int head_dim, int block_size);
+int attn_block_router_tail(const void* q, const void* k, const void* v, int dtype, int n,
+                           int heads, int head_dim, const uint8_t* seg, int protected_prefix_len,
+                           int block_size, int k_sel, float scale, int32_t* tiles, int32_t* prot,
+                           int n_prot, float* tail_lse, float* tail_v,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention with the pooled tail term.
+ * attn_block_sparse, where every query row of block qb also attends one extra
+ * key with logit tail_lse[h][qb] and value tail_v[h][qb][:] (from
+ * attn_block_router_tail with the same scale), so nothing leaves the softmax;
+ * a -inf logit adds nothing. Workspace as attn_block_sparse.
+ * Errors: as attn_block_sparse, plus H3_EINVAL for null tail_lse or tail_v.
+ */
+int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtype,
+                           int n, int heads, int head_dim,
+                           const uint8_t* seg, const float* t,
+                           float strength, float window, float falloff, float cap, float scale,
+                           int block_size, const int32_t* tiles, int k_sel,
+                           const int32_t* prot, int n_prot,
+                           const float* tail_lse, const float* tail_v,
+                           void* o, int o_dtype, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Stable LSE merge of one partition result into an accumulator, in place.
  * From "Flash Partitions for H3 native temporal alignment", section 4:
  *   adjusted_L = lse_i + log_w (+ log_w_rows[row][h] when non-NULL),

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     assert set(names) == set(api.EXPORTS)
     L = api.lib()
     for n in names:
@@ -215,3 +215,23 @@ def test_via_argument_checks_and_workspace():
     bad = list(args)
     bad[6] = 48
     assert L.attn_dense_tara_via(*bad, None, 0, None) == -2
+
+
+def test_tail_entry_points_reject_bad_arguments():
+    """Routing and sparse attention with the tail term: argument checks before any HIP
+    call; the router workspace grows by one float32 mean per (head, block, d)."""
+    L = api.lib()
+    P = ctypes.c_void_p(16)
+    nb = (1000 + 63) // 64
+    assert (L.attn_block_router_tail_workspace(1000, 2, 64, 64)
+            == L.attn_block_router_workspace(1000, 2, 64, 64) + _a256(nb * 2 * 64 * 4))
+    base = [P, P, P, 1, 1000, 2, 64, P, 0, 64, 4, 0.125, P, P, 1, P, P]
+    assert L.attn_block_router_tail(*base, None, 0, None) == -4
+    for i, bad in ((2, None), (15, None), (16, None), (11, 0.0), (11, float("nan"))):
+        args = list(base)
+        args[i] = bad
+        assert L.attn_block_router_tail(*args, None, 0, None) == -1, i
+    sp = [P, P, P, 1, 1000, 2, 64, P, P, 2.0, 0.2, 0.25, 6.0, 0.125, 64, P, 4, P, 1]
+    assert L.attn_block_sparse_tail(*sp, None, P, P, 1, P, P, 1 << 30, None) == -1
+    assert L.attn_block_sparse_tail(*sp, P, None, P, 1, P, P, 1 << 30, None) == -1
+    assert L.attn_block_sparse_tail(*sp, P, P, P, 1, P, None, 0, None) == -4

@@ -141,3 +141,40 @@ def test_p1_shape_dense_tara_sampled(micro, path):
     o_ref, l_ref = _dense_ref(wl, seg, t, host, rows)
     ri = torch.from_numpy(rows).cuda()
     compare(o[ri][:, P1_HEADS], lse[ri][:, P1_HEADS], o_ref, l_ref, "bf16", f"p1 shape {path}")
+
+
+def test_full_sparse_with_tail_sampled(full):
+    """Full scale, s = 0.90, TARA on routed guide tiles plus the pooled tail key: tail
+    terms of the sampled heads against the oracle, outputs on sampled rows."""
+    wl, seg, t, dev, host, host32 = full
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.90)
+    print("router + tail 116883 x 56, s=0.90", flush=True)
+    tiles, prot, tl, tv = api.attn_block_router_tail(dev["q"], dev["k"], dev["v"], dev["seg"],
+                                                     wl.protected_prefix_len, plan["k_sel"],
+                                                     plan["n_prot"], scale=wl.scale)
+    o, lse = api.attn_block_sparse_tail(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], tiles,
+                                        prot, tl, tv, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    tl_np = tiles.cpu().numpy()
+    tails = {}
+    for j, h in enumerate(HEADS):
+        tails[j] = oracle.tail_terms(host32["q"][:, j], host32["k"][:, j], host["v"][:, j], seg,
+                                     wl.protected_prefix_len, 64, tl_np[h], wl.scale)
+        fin = np.isfinite(tails[j][0])
+        el = float(np.max(np.abs(tl[h].cpu().numpy()[fin] - tails[j][0][fin])))
+        ev = float(np.max(np.abs(tv[h].cpu().numpy() - tails[j][1])))
+        print(f"[full tail terms head {h}] lse err {el:.2e} v err {ev:.2e}", flush=True)
+        assert el < 1e-3 and ev < 1e-3
+    blocks = _blocks()
+    ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64,
+                              prot.cpu().numpy(), tl_np[HEADS], heads=range(3), qblocks=blocks,
+                              tails=tails)
+    og, lg, orf, lrf = [], [], [], []
+    for (j, qb), (ob, lb) in ref.items():
+        lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
+        og.append(o[lo:hi, HEADS[j]])
+        lg.append(lse[lo:hi, HEADS[j]])
+        orf.append(ob)
+        lrf.append(lb)
+    compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
+            "full sparse tail s=0.9")

@@ -287,6 +287,103 @@ def test_sparse_hand_built_lists(d, dtype):
     compare(o, lse, o_ref, l_ref, dtype, f"sparse hand lists d={d} {dtype}")
 
 
+# ------------------------------------------------------------------- tail term
+
+def _tails_oracle(wl, q, k, v, seg, tiles, heads):
+    """oracle.tail_terms for the given heads: {j: (lse [nqb], v [nqb, d])}."""
+    out = {}
+    for j, h in enumerate(heads):
+        out[j] = oracle.tail_terms(W.to_float32(q[:, h], wl.dtype), W.to_float32(k[:, h], wl.dtype),
+                                   f64(v[:, h], wl.dtype), seg, wl.protected_prefix_len, 64,
+                                   tiles[h], wl.scale)
+    return out
+
+
+def test_router_tail_terms_mid():
+    """31,552 rows, 24 heads, s = 0.85: the tail logit and value of every query block of
+    three heads against the oracle; the tile lists are those of the plain router."""
+    wl = W.MID_SPARSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.85)
+    tiles0, _ = api.attn_block_router(qd, kd, seg_d, wl.protected_prefix_len, plan["k_sel"],
+                                      plan["n_prot"])
+    tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, wl.protected_prefix_len,
+                                                     plan["k_sel"], plan["n_prot"], scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(tiles, tiles0)
+    heads = [0, 11, 23]
+    ref = _tails_oracle(wl, q, k, v, seg, tiles.cpu().numpy(), heads)
+    tl, tv = tl.cpu().numpy(), tv.cpu().numpy()
+    for j, h in enumerate(heads):
+        l_ref, v_ref = ref[j]
+        assert np.array_equal(np.isneginf(tl[h]), np.isneginf(l_ref))
+        fin = np.isfinite(l_ref)
+        el = float(np.max(np.abs(tl[h][fin] - l_ref[fin])))
+        ev = float(np.max(np.abs(tv[h] - v_ref)))
+        print(f"[tail terms head {h}] lse err {el:.2e} v err {ev:.2e}", flush=True)
+        assert el < 1e-3 and ev < 1e-3
+
+
+@pytest.mark.parametrize("dtype,sparsity", [("bf16", 0.5), ("bf16", 0.9), ("f32", 0.7)])
+def test_sparse_with_tail_small(dtype, sparsity):
+    """Routed tiles with the TARA penalty plus the pooled tail key; every output row
+    against the oracle."""
+    d = 128 if dtype == "bf16" else 64
+    wl = W.custom("sp_tail", [W.Span(W.SEG_TEXT, 100), W.Span(W.SEG_GUIDE, 8 * 130, 8),
+                              W.Span(W.SEG_AUDIO, 60), W.Span(W.SEG_OUTPUT, 8 * 130, 8)],
+                  heads=3, head_dim=d, dtype=dtype, seed_index=91, frame_weight=0.7,
+                  protected_prefix_len=100)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    plan = api.router_plan(seg, 100, sparsity)
+    print(f"case tail {dtype} s={sparsity}", flush=True)
+    tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, 100, plan["k_sel"],
+                                                     plan["n_prot"], scale=wl.scale)
+    o, lse = api.attn_block_sparse_tail(qd, kd, vd, seg_d, t_d, tiles, prot, tl, tv, *wl.tara,
+                                        scale=wl.scale)
+    torch.cuda.synchronize()
+    tiles_np = tiles.cpu().numpy()
+    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3))
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, 64, prot.cpu().numpy(), tiles_np, tails=tails)
+    o_ref = np.zeros((wl.n, 3, d))
+    l_ref = np.zeros((wl.n, 3))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * 64:qb * 64 + len(ob), h] = ob
+        l_ref[qb * 64:qb * 64 + len(ob), h] = lb
+    compare(o, lse, o_ref, l_ref, dtype, f"sparse tail {dtype} s={sparsity}")
+
+
+def test_sparse_tail_equals_dense_for_constant_blocks():
+    """Rows identical inside every 64-row block, no penalty: the pooled tail key stands in
+    exactly for the left-out tiles, so sparse + tail on the GPU reproduces dense
+    attention (the oracle's) within the bf16 tolerance; without the tail it does not."""
+    wl = W.custom("const_blocks", [W.Span(W.SEG_TEXT, 64), W.Span(W.SEG_GUIDE, 12 * 64, 12),
+                                   W.Span(W.SEG_OUTPUT, 12 * 64 + 37, 12)],
+                  heads=2, head_dim=128, dtype="bf16", seed_index=92, strength=0.0,
+                  protected_prefix_len=64)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    nb = (wl.n + 63) // 64
+    rep = np.minimum(np.arange(wl.n) // 64 * 64, wl.n - 1)
+    q, k, v = q[rep], k[rep], v[rep]        # every row repeats its block's first row
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, 64, 0.75)
+    tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, 64, plan["k_sel"],
+                                                     plan["n_prot"], scale=wl.scale)
+    o, lse = api.attn_block_sparse_tail(qd, kd, vd, seg_d, t_d, tiles, prot, tl, tv, *wl.tara,
+                                        scale=wl.scale)
+    o0, l0 = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, seg,
+                                     t, wl.tara, wl.scale)
+    compare(o, lse, o_ref, l_ref, "bf16", "sparse tail vs dense (constant blocks)")
+    assert float(np.max(np.abs(l0.cpu().numpy() - l_ref))) > 1e-2
+
+
 # ------------------------------------------------------------------- merge
 
 def test_lse_merge_matches_oracle():
