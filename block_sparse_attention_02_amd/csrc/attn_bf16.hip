@@ -21,10 +21,11 @@
 // Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
 // lane holds one query column; softmax row reductions stay in registers plus one
 // exchange between lane halves.
-// K and V^T tiles are double-buffered in LDS in rows padded by 16 bytes (bank-conflict-
-// free operand reads, and every operand address is one base register plus an immediate)
-// and loaded ahead straight from global memory into LDS (buffer_load ... lds), so the
-// loads hold no registers.
+// K and V^T tiles sit in three LDS stages each, in rows padded by 16 bytes (bank-
+// conflict-free operand reads, and every operand address is one base register plus an
+// immediate), and are loaded ahead straight from global memory into LDS (buffer_load
+// ... lds), so the loads hold no registers. The two waves of a SIMD run one slot apart:
+// one wave's matrix products overlap the other's softmax.
 // V^T comes from a transposed copy of v whose keys are permuted within 16-key groups
 // (bits 2 and 3 of the key index swapped) so that the probability registers produced by
 // the first product are directly the B operand of the second.
