@@ -23,11 +23,11 @@ from .tara import (tara_penalty, tara_bias, dense_tara, plain_attention, lse_mer
                    tara_partitions, runs)
 from .router import (router_plan, select_count, block_means_fp32, pooled_scores_fp32,
                      select_topk, route_head)
-from .sparse import block_sparse_block, block_sparse, tail_terms
+from .sparse import block_sparse_block, block_sparse, tail_terms, is_sink_block
 
 __all__ = [
     "tara_penalty", "tara_bias", "dense_tara", "plain_attention", "lse_merge",
     "tara_partitions", "runs", "router_plan", "select_count", "block_means_fp32",
     "pooled_scores_fp32", "select_topk", "route_head", "block_sparse_block", "block_sparse",
-    "tail_terms",
+    "tail_terms", "is_sink_block",
 ]

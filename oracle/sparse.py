@@ -19,6 +19,18 @@ S is the router's float32 pooled score (unscaled q-mean . k-mean), n_u the rows 
 tile u and vbar_u the mean of its V rows: every left-out key is stood in for by
 its tile's centroids. It is one extra key of every row of the block; the TARA
 penalty, like the routing, does not see it. With no unrouted tile it vanishes.
+
+Block size: the same definitions hold for 32-, 64- and 128-row blocks ("H3 SLA
+Attention", inputs table, block_size: the number of rows that share one key
+selection; halving it doubles the block count and keeps the attention work).
+Query blocks and key blocks have the same size.
+
+Sink queries ("Per-layer attention config LoRAs", section "Experimental:
+audio/text protection": the audio queries are kept fully exact, sink_queries =
+audio): a query block holding any row of a sink segment attends every key of the
+sequence. Reading: the whole block is dense,
+including its few non-sink rows at a segment boundary, and it has no tail term
+since nothing is left out.
 """
 from __future__ import annotations
 
@@ -61,8 +73,14 @@ def tail_terms(q32_h, k32_h, v_h, seg, protected_prefix_len, block_size, tiles_h
     return lse, vt
 
 
+def is_sink_block(seg, block_size, qb, sink_segments):
+    """Whether query block ``qb`` holds a row of any segment in ``sink_segments``."""
+    lo, hi = qb * block_size, min(len(seg), (qb + 1) * block_size)
+    return any(int(x) in set(sink_segments) for x in np.asarray(seg)[lo:hi])
+
+
 def block_sparse_block(q_h, k_h, v_h, seg, t, params, scale, block_size, prot, tiles_row, qb,
-                       tail=None):
+                       tail=None, sink_segments=()):
     """Output rows of query block ``qb`` for one head.
 
     q_h, k_h, v_h: [n, d] float64. ``prot``: protected block indices;
@@ -72,12 +90,18 @@ def block_sparse_block(q_h, k_h, v_h, seg, t, params, scale, block_size, prot, t
     softmax runs over those keys only, with the dense TARA score
     s_ij = scale * q_i . k_j - p_ij. ``tail`` = (L_tail, v_tail) of this block
     adds one key with logit L_tail and value v_tail to every row (see
-    ``tail_terms``). Returns (o [rows, d], lse [rows]).
+    ``tail_terms``). A query block holding a row of a segment in
+    ``sink_segments`` attends every key and takes no tail. Returns (o [rows, d],
+    lse [rows]).
     """
     n = q_h.shape[0]
     nb = (n + block_size - 1) // block_size
     lo, hi = qb * block_size, min(n, (qb + 1) * block_size)
-    blocks = sorted({int(b) for b in list(prot) + list(tiles_row) if 0 <= int(b) < nb})
+    if sink_segments and is_sink_block(seg, block_size, qb, sink_segments):
+        blocks = list(range(nb))
+        tail = None
+    else:
+        blocks = sorted({int(b) for b in list(prot) + list(tiles_row) if 0 <= int(b) < nb})
     keys = (np.concatenate([np.arange(b * block_size, min(n, (b + 1) * block_size))
                             for b in blocks]) if blocks else np.zeros(0, dtype=np.int64))
     s = scale * (q_h[lo:hi] @ k_h[keys].T) - tara_bias(seg[lo:hi], t[lo:hi], seg[keys],
@@ -92,12 +116,13 @@ def block_sparse_block(q_h, k_h, v_h, seg, t, params, scale, block_size, prot, t
 
 
 def block_sparse(q, k, v, seg, t, params, scale, block_size, prot, tiles, heads=None,
-                 qblocks=None, tails=None):
+                 qblocks=None, tails=None, sink_segments=()):
     """Block-sparse outputs for the selected heads and query blocks.
 
     q, k, v: [n, H, d] float64; tiles: [H, nqb, k_sel]; tails: optional
-    {h: (L_tail [nqb], v_tail [nqb, d])}. Returns {(h, qb): (o_rows, lse_rows)} for
-    every requested pair.
+    {h: (L_tail [nqb], v_tail [nqb, d])}; sink_segments: segment ids whose query
+    blocks attend densely. Returns {(h, qb): (o_rows, lse_rows)} for every
+    requested pair.
     """
     n, H, d = q.shape
     nqb = (n + block_size - 1) // block_size
@@ -111,5 +136,6 @@ def block_sparse(q, k, v, seg, t, params, scale, block_size, prot, tiles, heads=
         for qb in qblocks:
             tail = None if tails is None else (tails[h][0][qb], tails[h][1][qb])
             out[(h, qb)] = block_sparse_block(qh, kh, vh, seg, t, params, scale, block_size,
-                                              prot, tiles[h][qb], qb, tail=tail)
+                                              prot, tiles[h][qb], qb, tail=tail,
+                                              sink_segments=sink_segments)
     return out

@@ -626,3 +626,102 @@ def test_tail_pin_catches_planted_mistakes():
     assert worst(True, True) < 1e-5
     assert worst(False, True) > 1e-3
     assert worst(True, False) > 1e-3
+
+
+# -------------------------------------------------------------- block sizes and sinks
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_router_plan_block_sizes_full_scale(bs):
+    """At block size 32 and 128 the protected blocks are those overlapping the text
+    span [0, 7259) or the audio span [61571, 62571) (closed form from the spans), and k
+    is the top (1 - sparsity) of the rest ("H3 SLA Attention", inputs table,
+    block_size: the same rule at a finer or coarser block)."""
+    seg, _ = W.layout(W.FULL_SPARSE)
+    n = W.FULL_SPARSE.n
+    nb_ref = -(-n // bs)
+    text = list(range(0, (7259 - 1) // bs + 1))
+    audio = list(range(61571 // bs, (62571 - 1) // bs + 1))
+    nb, prot, vid, k = oracle.router_plan(seg, 7259, bs, 0.90)
+    assert nb == nb_ref
+    assert list(prot) == text + audio
+    assert len(vid) == nb_ref - len(text) - len(audio)
+    assert k == math.ceil(0.1 * len(vid) - 1e-9)
+    assert (nb, len(prot), len(vid), k) == {32: (3653, 259, 3394, 340),
+                                             128: (914, 65, 849, 85)}[bs]
+
+
+def test_sparse_block_size_nesting():
+    """A block of 2b rows with key list T gives the same rows as its two b-row halves,
+    each with the halves of T (and of the protected list): the block size only
+    changes how finely keys are selected."""
+    wl, seg, t, q, k, v = _sparse_case(seed=310)
+    n = wl.n
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    rng = np.random.default_rng(5)
+    for big in (32, 64):
+        small = big // 2
+        nbb = -(-n // big)
+        prot = np.array([0, 3])
+        for qb in range(nbb):
+            lst = rng.choice(nbb, 4, replace=False)
+            ob, lb = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t, wl.tara,
+                                               wl.scale, big, prot, lst, qb)
+            halves = [2 * x + y for x in lst for y in (0, 1)]
+            hprot = [2 * x + y for x in prot for y in (0, 1)]
+            parts_o, parts_l = [], []
+            for sub in (2 * qb, 2 * qb + 1):
+                if sub * small >= n:
+                    continue
+                o2, l2 = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t,
+                                                   wl.tara, wl.scale, small, hprot, halves, sub)
+                parts_o.append(o2)
+                parts_l.append(l2)
+            assert np.max(np.abs(ob - np.concatenate(parts_o))) < 1e-12
+            assert np.max(np.abs(lb - np.concatenate(parts_l))) < 1e-12
+
+
+def test_sparse_block_32_brute_force():
+    """Block size 32: scalar loops over the listed 32-row key blocks."""
+    wl, seg, t, q, k, v = _sparse_case(seed=311)
+    n = wl.n
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    prot = np.array([1])
+    for qb, lst in ((0, [4, 7]), (5, [0, 2]), ((n - 1) // 32, [3, (n - 1) // 32])):
+        ob, lb = oracle.block_sparse_block(q64[:, 1], k64[:, 1], v64[:, 1], seg, t, wl.tara,
+                                           wl.scale, 32, prot, np.array(lst), qb)
+        keys = np.array([r for b in sorted({1, *lst}) for r in range(32 * b, 32 * b + 32)
+                         if r < n])
+        rows = range(32 * qb, min(n, 32 * qb + 32))
+        ref_o, ref_l = _brute_dense_rows(q64[:, 1], k64[:, 1], v64[:, 1], seg, t, wl.tara,
+                                        wl.scale, rows, keys)
+        assert np.max(np.abs(ob - ref_o)) < 1e-12 and np.max(np.abs(lb - ref_l)) < 1e-12
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_sink_query_blocks_attend_every_key(bs):
+    """With audio sink queries, a query block holding any audio row equals dense TARA
+    on its rows and ignores a tail term; every other block is unchanged."""
+    wl, seg, t, q, k, v = _sparse_case(seed=312)
+    n = wl.n
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    o_d, l_d = oracle.dense_tara(q64, k64, v64, seg, t, seg, t, wl.tara, wl.scale)
+    nb = -(-n // bs)
+    audio_rows = np.nonzero(seg == W.SEG_AUDIO)[0]
+    sinks = set(int(r) // bs for r in audio_rows)
+    assert sinks and len(sinks) < nb
+    prot = np.array([0])
+    lst = np.array([nb - 1])
+    tail = (0.5, np.ones(wl.head_dim))
+    for qb in range(nb):
+        assert oracle.is_sink_block(seg, bs, qb, (W.SEG_AUDIO,)) == (qb in sinks)
+        lo, hi = qb * bs, min(n, qb * bs + bs)
+        got = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t, wl.tara,
+                                        wl.scale, bs, prot, lst, qb, tail=tail,
+                                        sink_segments=(W.SEG_AUDIO,))
+        plain = oracle.block_sparse_block(q64[:, 0], k64[:, 0], v64[:, 0], seg, t, wl.tara,
+                                          wl.scale, bs, prot, lst, qb, tail=tail)
+        if qb in sinks:
+            assert np.max(np.abs(got[0] - o_d[lo:hi, 0])) < 1e-12
+            assert np.max(np.abs(got[1] - l_d[lo:hi, 0])) < 1e-12
+        else:
+            assert np.array_equal(got[0], plain[0]) and np.array_equal(got[1], plain[1])
