@@ -26,6 +26,7 @@ EXPORTS = (
     "attn_router_plan", "attn_block_router_workspace", "attn_block_router",
     "attn_block_sparse_workspace", "attn_block_sparse",
     "attn_block_router_tail_workspace", "attn_block_router_tail", "attn_block_sparse_tail",
+    "attn_block_sparse_sinks",
     "partition_lse_merge",
     "attn_dense_tara_via_workspace", "attn_dense_tara_via",
 )
@@ -50,6 +51,9 @@ _SIGS = {
     "attn_block_sparse_tail": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f,
                                     _f, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _sz,
                                     _vp]),
+    "attn_block_sparse_sinks": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f,
+                                     _f, _i, _vp, _i, _vp, _i, _vp, _vp, ctypes.c_uint, _vp,
+                                     _i, _vp, _vp, _sz, _vp]),
     "partition_lse_merge": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _vp]),
     "attn_dense_tara_via_workspace": (_sz, [_vp, _vp, _i, _i, _i, _i]),
     "attn_dense_tara_via": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -292,6 +296,38 @@ def attn_block_sparse_tail(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, stren
                                       _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
                                       _stream(stream))
     _check("attn_block_sparse_tail", st)
+    return o, lse
+
+
+def attn_block_sparse_sinks(q, k, v, seg, t, tiles, prot, sink_segments, tail_lse=None,
+                            tail_v=None, strength=2.0, window=0.20, falloff=0.25, cap=6.0,
+                            scale=None, block_size=64, o=None, o_dtype=None, lse=None, ws=None,
+                            stream=None):
+    """Block-sparse attention where query blocks holding a row of a segment in the bit
+    mask ``sink_segments`` attend every key; optional tail terms: returns (o, lse)."""
+    import torch
+    n, H, D = q.shape
+    dt = _dtype_code(q)
+    k_sel = int(tiles.shape[-1]) if tiles is not None else 0
+    n_prot = int(prot.numel()) if prot is not None else 0
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if ws is None:
+        ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
+    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    st = lib().attn_block_sparse_sinks(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg),
+                                       _ptr(t), strength, window, falloff, cap, scale, block_size,
+                                       _ptr(tiles) if k_sel > 0 else None, k_sel,
+                                       _ptr(prot) if n_prot > 0 else None, n_prot,
+                                       _ptr(tail_lse) if tail_lse is not None else None,
+                                       _ptr(tail_v) if tail_v is not None else None,
+                                       int(sink_segments), _ptr(o), _dtype_code(o), _ptr(lse),
+                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check("attn_block_sparse_sinks", st)
     return o, lse
 
 

@@ -27,6 +27,12 @@ int check_tara(float strength, float window, float falloff, float cap, float sca
 
 bool dtype_ok(int dt) { return dt == H3_DTYPE_F32 || dt == H3_DTYPE_BF16; }
 bool dim_ok(int d) { return d == 64 || d == 128; }
+bool bs_ok(int bs) { return bs == 32 || bs == 64 || bs == 128; }
+// Sequences the router and the block-sparse kernels take: at most kMaxBlocks blocks of
+// the routing size and at most kMaxBlocks 64-row tiles.
+bool blocks_ok(int n, int bs) {
+  return (n + bs - 1) / bs <= kMaxBlocks && (n + kTile - 1) / kTile <= kMaxBlocks;
+}
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -52,6 +58,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, 
   a.scale = scale;
   a.strength = strength; a.window = window; a.inv_falloff = 1.f / falloff; a.cap = cap;
   a.prot = nullptr; a.n_prot = 0; a.tiles = nullptr; a.k_sel = 0; a.nqb = 0;
+  a.bs = kTile; a.sink_mask = 0u;
   a.tail_lse = nullptr; a.tail_v = nullptr;
   return a;
 }
@@ -223,11 +230,11 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
   if (protected_prefix_len < 0 || protected_prefix_len > n) return H3_EINVAL;
   if (!std::isfinite(sparsity_ratio) || sparsity_ratio < 0.0 || sparsity_ratio >= 1.0)
     return H3_EINVAL;
-  if (block_size != kTile) return H3_EUNSUPPORTED;
-  const int blocks = (n + kTile - 1) / kTile;
+  if (!bs_ok(block_size)) return H3_EUNSUPPORTED;
+  const int blocks = (n + block_size - 1) / block_size;
   int prot = 0;
   for (int b = 0; b < blocks; ++b) {
-    const int lo = b * kTile, hi = std::min(n, lo + kTile);
+    const int lo = b * block_size, hi = std::min(n, lo + block_size);
     bool p = lo < protected_prefix_len;
     for (int r = lo; r < hi && !p; ++r)
       p = seg_host[r] == H3_SEG_TEXT || seg_host[r] == H3_SEG_AUDIO;
@@ -251,13 +258,13 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
 }
 
 size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size) {
-  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || block_size != kTile) return 0;
-  return router_ws_bytes(n, heads, head_dim, false);
+  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || !bs_ok(block_size)) return 0;
+  return router_ws_bytes(n, heads, head_dim, block_size, false);
 }
 
 size_t attn_block_router_tail_workspace(int n, int heads, int head_dim, int block_size) {
-  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || block_size != kTile) return 0;
-  return router_ws_bytes(n, heads, head_dim, true);
+  if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || !bs_ok(block_size)) return 0;
+  return router_ws_bytes(n, heads, head_dim, block_size, true);
 }
 
 }  // extern "C"
@@ -274,16 +281,16 @@ int route(const void* q, const void* k, const void* v, int dtype, int n, int hea
   if (protected_prefix_len < 0 || protected_prefix_len > n) return H3_EINVAL;
   if (k_sel < 0 || n_prot < 0 || (k_sel > 0 && !tiles) || (n_prot > 0 && !prot))
     return H3_EINVAL;
-  if (!dtype_ok(dtype) || !dim_ok(head_dim) || block_size != kTile || heads > 65535)
+  if (!dtype_ok(dtype) || !dim_ok(head_dim) || !bs_ok(block_size) || heads > 65535)
     return H3_EUNSUPPORTED;
-  const int nb = (n + kTile - 1) / kTile;
+  const int nb = (n + block_size - 1) / block_size;
   if (k_sel > nb) return H3_EINVAL;
-  if (nb > router_max_blocks()) return H3_EUNSUPPORTED;
-  const size_t need = router_ws_bytes(n, heads, head_dim, tail);
+  if (!blocks_ok(n, block_size) || nb > router_max_blocks()) return H3_EUNSUPPORTED;
+  const size_t need = router_ws_bytes(n, heads, head_dim, block_size, tail);
   if (!ws || ws_bytes < need) return H3_EWORKSPACE;
-  RouterWs w = router_ws_carve(ws, n, heads, head_dim, tail);
-  hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, seg,
-                               protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
+  RouterWs w = router_ws_carve(ws, n, heads, head_dim, block_size, tail);
+  hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, block_size,
+                               seg, protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
                                tail ? tail_lse : nullptr, tail ? tail_v : nullptr,
                                (hipStream_t)stream);
   return e == hipSuccess ? H3_OK : H3_ELAUNCH;
@@ -293,17 +300,18 @@ int sparse(const void* q, const void* k, const void* v, int dtype, int n, int he
            int head_dim, const uint8_t* seg, const float* t, float strength, float window,
            float falloff, float cap, float scale, int block_size, const int32_t* tiles,
            int k_sel, const int32_t* prot, int n_prot, const float* tail_lse,
-           const float* tail_v, void* o, int o_dtype, float* lse, void* ws, size_t ws_bytes,
-           void* stream) {
+           const float* tail_v, uint32_t sink_mask, void* o, int o_dtype, float* lse, void* ws,
+           size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !seg || !t || !o || !lse) return H3_EINVAL;
   if (n <= 0 || heads <= 0) return H3_EINVAL;
   if (k_sel < 0 || n_prot < 0 || k_sel + n_prot == 0) return H3_EINVAL;
   if ((k_sel > 0 && !tiles) || (n_prot > 0 && !prot)) return H3_EINVAL;
   if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
-  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || block_size != kTile ||
+  if (sink_mask & ~0xFu) return H3_EINVAL;  // segment ids are 0..3
+  if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || !bs_ok(block_size) ||
       heads > 65535)
     return H3_EUNSUPPORTED;
-  if ((n + kTile - 1) / kTile > kMaxBlocks) return H3_EUNSUPPORTED;
+  if (!blocks_ok(n, block_size)) return H3_EUNSUPPORTED;
   const size_t need = attn_dense_tara_workspace(n, heads, head_dim, dtype);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
   AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
@@ -312,7 +320,9 @@ int sparse(const void* q, const void* k, const void* v, int dtype, int n, int he
   a.n_prot = n_prot;
   a.tiles = tiles;
   a.k_sel = k_sel;
-  a.nqb = (n + kTile - 1) / kTile;
+  a.nqb = (n + block_size - 1) / block_size;
+  a.bs = block_size;
+  a.sink_mask = sink_mask;
   a.tail_lse = tail_lse;
   a.tail_v = tail_v;
   const bool pen = strength > 0.f && cap > 0.f;
@@ -351,8 +361,8 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, in
                       const int32_t* tiles, int k_sel, const int32_t* prot, int n_prot, void* o,
                       int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
-                scale, block_size, tiles, k_sel, prot, n_prot, nullptr, nullptr, o, o_dtype, lse,
-                ws, ws_bytes, stream);
+                scale, block_size, tiles, k_sel, prot, n_prot, nullptr, nullptr, 0u, o, o_dtype,
+                lse, ws, ws_bytes, stream);
 }
 
 int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtype, int n,
@@ -363,8 +373,21 @@ int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtyp
                            int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!tail_lse || !tail_v) return H3_EINVAL;
   return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
-                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v, o, o_dtype, lse,
-                ws, ws_bytes, stream);
+                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v, 0u, o, o_dtype,
+                lse, ws, ws_bytes, stream);
+}
+
+int attn_block_sparse_sinks(const void* q, const void* k, const void* v, int dtype, int n,
+                            int heads, int head_dim, const uint8_t* seg, const float* t,
+                            float strength, float window, float falloff, float cap, float scale,
+                            int block_size, const int32_t* tiles, int k_sel,
+                            const int32_t* prot, int n_prot, const float* tail_lse,
+                            const float* tail_v, unsigned sink_segments, void* o, int o_dtype,
+                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if ((tail_lse == nullptr) != (tail_v == nullptr)) return H3_EINVAL;
+  return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
+                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v,
+                (uint32_t)sink_segments, o, o_dtype, lse, ws, ws_bytes, stream);
 }
 
 int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

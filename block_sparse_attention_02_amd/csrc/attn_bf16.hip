@@ -202,7 +202,9 @@ __device__ __forceinline__ float pair_sum_swap(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool SPARSE, bool PEN>
+// FINE: block-sparse with 32-row routing blocks (per-wave lists, half tiles); a
+// separate instance so the 64/128-row kernel carries none of that code.
+template <int D, bool SPARSE, bool PEN, bool FINE = false>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NW = 8;               // waves per workgroup (two per SIMD)
   constexpr int BM = 32 * NW;         // query rows per workgroup
@@ -226,8 +228,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ uint8_t kseg0[64], kseg1[64], kseg2[64];
   __shared__ float kt0[64], kt1[64], kt2[64];
   __shared__ int simd_waves[4];
-  // sparse: bitmap 0 = protected tiles, bitmap 1 + j = routed tiles of query block j
-  __shared__ uint32_t tile_bits[SPARSE ? (QB + 1) * kBitmapWords : 1];
+  __shared__ int sink_waves;  // sparse: bit w = wave w's rows hold a sink-segment row
+  // sparse: bitmap 0 = protected blocks, bitmap 1 + j = routed blocks of map j (see below)
+  __shared__ uint32_t tile_bits[SPARSE ? (NW + 1) * kBitmapWords : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,8 +264,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   // ---- the two waves that share a SIMD take opposite phases (group 0 / group 1):
   // while one runs its matrix-core slot the other runs its softmax slot.
   if (tid < 4) simd_waves[tid] = 0;
-  // does any query row of this workgroup take the penalty? (also orders the reset above)
+  if (SPARSE && tid == 0) sink_waves = 0;
+  // does any query row of this workgroup take the penalty? (also orders the resets above)
   const bool pen_wg = __syncthreads_or(q_out);
+  if constexpr (SPARSE) {
+    const bool sink_row = qvalid && ((a.sink_mask >> a.q_seg[qrow]) & 1u);
+    if (__ballot(sink_row) != 0ull && lane == 0) atomicOr(&sink_waves, 1 << wave);
+  }
   int grp = 0;
   if (lane == 0) {
     const int simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);  // HW_ID.SIMD_ID
@@ -273,31 +281,55 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   const int nkb = (a.nk + 63) / 64;
   const int ntiles = nkb;  // tiles are visited in ascending order; the cursor skips
                            // the ones no wave of this workgroup attends
-  // query blocks of this workgroup that exist (bit j = block QB*qblk + j)
-  int qb_valid = 0;
-  // this wave's bit in a tile's attend mask
-  const int my_qbit = 1 << (wave * 32 / kTile);
+  // A tile's attend mask has two bits per wave: bit 2w for keys 0-31 of the tile, bit
+  // 2w+1 for keys 32-63. Dense launches attend everything. Sparse launches keep one
+  // bitmap of protected blocks and one per "map" of routed blocks:
+  //   block size 64 / 128: map j = the 64-row block j of the workgroup (waves 2j, 2j+1),
+  //     one bit per 64-key tile (a 128-row block sets both of its tiles, and its two
+  //     64-row halves read the same list);
+  //   block size 32: map j = wave j's 32-row block, one bit per 32 keys, so a wave may
+  //     attend one half of a tile.
+  // A query block holding a row of a sink segment attends every key.
+  constexpr bool fine = SPARSE && FINE;
+  int map_valid = 0;     // bit j: map j's query block exists
+  bool my_sink = false;  // this wave's query block attends every key
+  const int my_shift = __builtin_amdgcn_readfirstlane(2 * wave);
   if constexpr (SPARSE) {
-    const int words = (nkb + 31) >> 5;  // the cursor reads no word past these
-    for (int i = tid; i < (QB + 1) * words; i += 64 * NW)
+    const int nmaps = fine ? NW : QB;
+    const int nbits = fine ? (a.nk + 31) >> 5 : nkb;
+    const int words = (nbits + 31) >> 5;  // the cursor reads no word past these
+    for (int i = tid; i < (nmaps + 1) * words; i += 64 * NW)
       tile_bits[(i / words) * kBitmapWords + i % words] = 0u;
     __syncthreads();
-    for (int i = tid; i < a.n_prot; i += 64 * NW) {
-      const int kb = a.prot[i];
-      if (kb >= 0 && kb < nkb) atomicOr(&tile_bits[kb >> 5], 1u << (kb & 31));
-    }
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const int qb = qblk * QB + j;
-      if (qb < a.nqb) {
-        qb_valid |= 1 << j;
-        const int32_t* lst = a.tiles + ((int64_t)h * a.nqb + qb) * a.k_sel;
-        for (int i = tid; i < a.k_sel; i += 64 * NW) {
-          const int kb = lst[i];
-          if (kb >= 0 && kb < nkb)
-            atomicOr(&tile_bits[(1 + j) * kBitmapWords + (kb >> 5)], 1u << (kb & 31));
+    const int sinks = sink_waves;
+    // marks routing block b (in units of the block size) in bitmap m
+    auto mark = [&](int m, int b) __attribute__((always_inline)) {
+      uint32_t* bm = tile_bits + m * kBitmapWords;
+      if (a.bs == 128) {
+        if (b >= 0 && b < (nkb + 1) / 2) {
+          atomicOr(&bm[(2 * b) >> 5], 1u << ((2 * b) & 31));
+          if (2 * b + 1 < nkb) atomicOr(&bm[(2 * b + 1) >> 5], 1u << ((2 * b + 1) & 31));
         }
+      } else if (b >= 0 && b < nbits) {
+        atomicOr(&bm[b >> 5], 1u << (b & 31));
       }
+    };
+    for (int i = tid; i < a.n_prot; i += 64 * NW) mark(0, a.prot[i]);
+    for (int j = 0; j < nmaps; ++j) {
+      const int row0 = qblk * BM + j * (fine ? 32 : 64);
+      if (row0 >= a.nq) continue;
+      map_valid |= 1 << j;
+      // waves of this map's query block (a 128-row block spans two maps)
+      const int wmask = fine ? (1 << j) : (a.bs == 128 ? 0xF << (4 * (j >> 1)) : 3 << (2 * j));
+      const bool sink = (sinks & wmask) != 0;
+      if (fine ? wave == j : (wave >> 1) == j) my_sink = sink;
+      if (sink) {
+        for (int i = tid; i < words; i += 64 * NW) tile_bits[(1 + j) * kBitmapWords + i] = ~0u;
+        continue;
+      }
+      const int qb = row0 / a.bs;
+      const int32_t* lst = a.tiles + ((int64_t)h * a.nqb + qb) * a.k_sel;
+      for (int i = tid; i < a.k_sel; i += 64 * NW) mark(1 + j, lst[i]);
     }
     __syncthreads();
   }
@@ -364,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   };
   // Walks the key tiles in ascending order, yielding those of one class that some
   // wave attends. Each wave examines 64 tiles at a time and keeps a ballot mask of
-  // the matching ones; .qmask says which query blocks attend the tile (sparse). Sparse
+  // the matching ones; .qmask is the tile's attend mask (two bits per wave). Sparse
   // launches load the summaries of the next 64 tiles one refill ahead, so a refill does
   // not wait on memory. Every wave walks the same sequence.
   struct Cursor {
@@ -392,17 +424,24 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       int qm = 0;
       if (kb < nkb) {
         if constexpr (SPARSE) {
-          const int w = kb >> 5;
-          const uint32_t b = 1u << (kb & 31);
-          if (tile_bits[w] & b) {
-            qm = qb_valid;
+          if constexpr (fine) {  // two bits per map and tile
+            const int w = kb >> 4, sh = 2 * (kb & 15);
+            const uint32_t p2 = tile_bits[w] >> sh;
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+              if ((map_valid >> j) & 1)
+                qm |= (int)((p2 | (tile_bits[(1 + j) * kBitmapWords + w] >> sh)) & 3u) << (2 * j);
           } else {
+            const int w = kb >> 5;
+            const uint32_t b = 1u << (kb & 31);
+            const bool pr = (tile_bits[w] & b) != 0u;
 #pragma unroll
             for (int j = 0; j < QB; ++j)
-              if (tile_bits[(1 + j) * kBitmapWords + w] & b) qm |= 1 << j;
+              if (((map_valid >> j) & 1) && (pr || (tile_bits[(1 + j) * kBitmapWords + w] & b)))
+                qm |= 0xF << (4 * j);
           }
         } else {
-          qm = 1;
+          qm = 0xFFFF;
         }
       }
       cu.mask = __ballot(qm != 0 && (is_fast(ti.flags) == want_fast));
@@ -418,14 +457,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
         cu.chunk * 64 + bit,
         fs & kTileFlagMask,
         __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t_lane), bit)),
-        SPARSE ? __builtin_amdgcn_readlane(cu.qm_lane, bit) : 1,
+        SPARSE ? __builtin_amdgcn_readlane(cu.qm_lane, bit) : 0xFFFF,
         want_fast ? 0.f
                   : __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(cu.t2_lane), bit)),
         fs >> 8};
   };
   // does this wave compute tile tl?
   auto attends = [&](const Tile& tl) __attribute__((always_inline)) -> bool {
-    return tl.kb < ntiles && (!SPARSE || (tl.qmask & my_qbit));
+    return tl.kb < ntiles && (!SPARSE || ((tl.qmask >> my_shift) & 3));
   };
 
   f32x16 oacc[DT];
@@ -472,16 +511,18 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   };
 
   // ---- softmax slot: scores with the penalty, online softmax, probabilities in bf16.
-  // p = exp2(s * cc + mb) for the 32 scores of this lane, as bf16 into pb; returns
-  // the float32 sum of the 32 (four chains).
-  auto exp_tile = [&](float cc, float mb) __attribute__((always_inline)) -> float {
+  // p = exp2(s * cc + mb) for the 32 scores of this lane, as bf16 into pb, with bias mb0
+  // for keys 0-31 of the tile and mb1 for keys 32-63 (-inf drops a half); returns the
+  // float32 sum of the 32 (four chains).
+  auto exp_tile = [&](float cc, float mb0, float mb1) __attribute__((always_inline)) -> float {
     float r[4];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       f32x8 pv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, mb));
+        pv[e] = __builtin_amdgcn_exp2f(
+            fmaf(sacc[s >> 1][8 * (s & 1) + e], cc, (s >> 1) ? mb1 : mb0));
         r[e & 3] = (s == 0 && e < 4) ? pv[e] : r[e & 3] + pv[e];
       }
       pb[s] = __builtin_convertvector(pv, bf16x8);
@@ -500,8 +541,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     l_run *= alpha;
     m_run = m_new;
   };
-  // maximum of this lane's 32 scores (a tree of three-input maxima)
-  auto score_max = [&]() __attribute__((always_inline)) -> float {
+  // maximum of this lane's scores in the kept halves of the tile (a tree of three-input
+  // maxima per half)
+  auto score_max = [&](bool keep0, bool keep1) __attribute__((always_inline)) -> float {
     float m[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -510,11 +552,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
           __builtin_elementwise_maximum(sacc[c][r], sacc[c][r + 1]),
           __builtin_elementwise_maximum(sacc[c][r + 2], sacc[c][r + 3]));
     }
-    return __builtin_elementwise_maximum(
-        __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[0], m[1]),
-                                      __builtin_elementwise_maximum(m[2], m[3])),
-        __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[4], m[5]),
-                                      __builtin_elementwise_maximum(m[6], m[7])));
+    const float m0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[0], m[1]),
+                                                   __builtin_elementwise_maximum(m[2], m[3]));
+    const float m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m[4], m[5]),
+                                                   __builtin_elementwise_maximum(m[6], m[7]));
+    return __builtin_elementwise_maximum(keep0 ? m0 : -INFINITY, keep1 ? m1 : -INFINITY);
   };
 
   // ---- softmax slot: scores with the penalty, online softmax, probabilities in bf16.
@@ -525,14 +567,20 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   auto softmax_slot = [&](auto general_tag, const uint8_t* ksg, const float* ktt,
                           const Tile& tl) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
+    // block size 32: this wave may attend only one half of the tile (keys 0-31 or 32-63);
+    // the other half gets a -inf bias
+    const int h2 = fine ? (tl.qmask >> my_shift) & 3 : 3;
+    const bool keep0 = h2 & 1, keep1 = h2 & 2;
     if constexpr (!GENERAL) {
       float bb = 0.f;
       if (PEN && pen_wg && (tl.flags & kTileUniformGuide) && q_out)
         bb = -tara_pen(fabsf(qt - tl.t), a.window, a.inv_falloff, a.strength, a.cap) * kLog2e;
-      float rs = exp_tile(c_log2, bb - m_run);
+      float mb = bb - m_run;
+      float rs = exp_tile(c_log2, keep0 ? mb : -INFINITY, keep1 ? mb : -INFINITY);
       if (__ballot(!(rs <= kRescaleSum)) != 0ull) {
-        raise_max(pair_max_swap(score_max() * c_log2 + bb));
-        rs = exp_tile(c_log2, bb - m_run);
+        raise_max(pair_max_swap(score_max(keep0, keep1) * c_log2 + bb));
+        mb = bb - m_run;
+        rs = exp_tile(c_log2, keep0 ? mb : -INFINITY, keep1 ? mb : -INFINITY);
       }
       l_run += rs;
     } else {
@@ -550,10 +598,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
         const int thr = tl.split - 4 * hh;  // key offset 32c + 8(r/4) + r%4 below thr: run A
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
+          const bool keep = c ? keep1 : keep0;
+          const float cA = keep ? bA : -INFINITY, cB = keep ? bB : -INFINITY;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kofs = 32 * c + 8 * (r >> 2) + (r & 3);
-            const float x = fmaf(sacc[c][r], c_log2, kofs < thr ? bA : bB);
+            const float x = fmaf(sacc[c][r], c_log2, kofs < thr ? cA : cB);
             sacc[c][r] = x;
             mx = __builtin_elementwise_maximum(mx, x);
           }
@@ -561,11 +611,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       } else {
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
+          const float hb = (c ? keep1 : keep0) ? 0.f : -INFINITY;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kl = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
             const uint32_t sg = ksg[kl];
-            float x = sacc[c][r] * c_log2;
+            float x = fmaf(sacc[c][r], c_log2, hb);
             if (sg == (uint32_t)kSegInvalid) {
               x = -INFINITY;
             } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
@@ -579,7 +630,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       }
       const float tmax = pair_max_swap(mx);
       if (__ballot(tmax > m_run + kLazyRescale) != 0ull) raise_max(tmax);
-      l_run += exp_tile(1.f, m_run == -INFINITY ? 0.f : -m_run);
+      const float mb = m_run == -INFINITY ? 0.f : -m_run;
+      l_run += exp_tile(1.f, mb, mb);
     }
   };
 
@@ -651,8 +703,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   // value tail_v, merged like any other key (log2 units here)
   float tail_w = 0.f;
   const float* tail_v = nullptr;
-  if (SPARSE && a.tail_lse && qvalid) {
-    const int64_t tb = (int64_t)h * a.nqb + qrow / kTile;
+  if (SPARSE && a.tail_lse && qvalid && !my_sink) {
+    const int64_t tb = (int64_t)h * a.nqb + qrow / a.bs;
     const float lt = a.tail_lse[tb] * kLog2e;
     if (lt != -INFINITY) {
       const float m_new = __builtin_elementwise_maximum(m_run, lt);
@@ -698,7 +750,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
 template <int D, bool SPARSE, bool PEN>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.nq + 255) / 256, a.H);
-  attn_bf16_kernel<D, SPARSE, PEN><<<grid, 512, 0, s>>>(a);
+  if constexpr (SPARSE) {
+    if (a.bs == 32) {
+      attn_bf16_kernel<D, true, PEN, true><<<grid, 512, 0, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  attn_bf16_kernel<D, SPARSE, PEN, false><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -18,8 +18,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float vsh[kSub][D];
   __shared__ uint32_t sgs[kSub];
   __shared__ float tss[kSub];
-  // sparse: the set of attended tiles (protected and routed) of this query block
-  __shared__ uint32_t tile_bits[SPARSE ? kBitmapWords : 1];
+  // sparse: the attended routing blocks (protected, routed, or all for a sink block) of
+  // the workgroup's query blocks: one map, or two for 32-row blocks (lanes 0-31, 32-63)
+  __shared__ uint32_t tile_bits[SPARSE ? 2 * kBitmapWords : 1];
+  __shared__ int sink_map[2];
 
   const int lane = threadIdx.x;
   const int qblk = blockIdx.x;
@@ -42,31 +44,54 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const bool q_out = PEN && qvalid && a.q_seg[qrow] == kSegOutput;
   float m = -INFINITY, l = 0.f;
 
-  const int nkb = (a.nk + 63) / 64;
+  // key blocks of the routing size (dense: 64-key units)
+  const int bs = SPARSE ? a.bs : 64;
+  const int nkb = (a.nk + bs - 1) / bs;
   const int words = (nkb + 31) >> 5;
+  const int nmaps = (SPARSE && bs == 32) ? 2 : 1;
+  const int my_map = nmaps == 2 ? lane >> 5 : 0;
   if constexpr (SPARSE) {
-    for (int i = lane; i < words; i += 64) tile_bits[i] = 0u;
+    for (int i = lane; i < 2 * kBitmapWords; i += 64) tile_bits[i] = 0u;
     __syncthreads();
-    const int32_t* rt = a.tiles + ((int64_t)h * a.nqb + qblk) * a.k_sel;
-    for (int i = lane; i < a.n_prot + a.k_sel; i += 64) {
-      const int kb = i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
-      if (kb >= 0 && kb < nkb) atomicOr(&tile_bits[kb >> 5], 1u << (kb & 31));
+    for (int m = 0; m < nmaps; ++m) {
+      const int row0 = qblk * 64 + m * 32;
+      if (row0 >= a.nq) continue;
+      const int qb = row0 / bs;
+      // a sink block attends every key (its rows may extend past this workgroup's)
+      const int lo = qb * bs, hi = min(a.nq, lo + bs);
+      bool sink_row = false;
+      for (int r = lo + lane; r < hi; r += 64) sink_row |= (a.sink_mask >> a.q_seg[r]) & 1u;
+      const bool sink = __ballot(sink_row) != 0ull;
+      if (lane == 0) sink_map[m] = sink;
+      uint32_t* bm = tile_bits + m * kBitmapWords;
+      if (sink) {
+        for (int i = lane; i < words; i += 64) bm[i] = ~0u;
+        continue;
+      }
+      const int32_t* rt = a.tiles + ((int64_t)h * a.nqb + qb) * a.k_sel;
+      for (int i = lane; i < a.n_prot + a.k_sel; i += 64) {
+        const int kb = i < a.n_prot ? a.prot[i] : rt[i - a.n_prot];
+        if (kb >= 0 && kb < nkb) atomicOr(&bm[kb >> 5], 1u << (kb & 31));
+      }
     }
     __syncthreads();
   }
 
-  // tiles in ascending order (sparse: only those in the set)
+  // key blocks in ascending order (sparse: those some lane attends; a lane masks the
+  // blocks its own query block does not attend)
   for (int kb = 0; kb < nkb; ++kb) {
+    bool mine = true;
     if constexpr (SPARSE) {
-      const uint32_t w = tile_bits[kb >> 5] >> (kb & 31);
+      const uint32_t w = (tile_bits[kb >> 5] | tile_bits[kBitmapWords + (kb >> 5)]) >> (kb & 31);
       if (w == 0u) {  // nothing further in this word
         kb = (kb | 31);
         continue;
       }
       kb += __builtin_ctz(w);
+      mine = (tile_bits[my_map * kBitmapWords + (kb >> 5)] >> (kb & 31)) & 1u;
     }
-    for (int sub = 0; sub < 64 / kSub; ++sub) {
-      const int k0 = kb * 64 + sub * kSub;
+    for (int sub = 0; sub < bs / kSub; ++sub) {
+      const int k0 = kb * bs + sub * kSub;
       if (k0 >= a.nk) break;
       __syncthreads();
       for (int e = lane; e < kSub * D; e += 64) {
@@ -92,7 +117,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         for (int d = 0; d < D; ++d) dot = fmaf(q[d], ksh[j][d], dot);
         float x = dot * a.scale;
         const uint32_t sg = sgs[j];
-        if (sg == (uint32_t)kSegInvalid) {
+        if (sg == (uint32_t)kSegInvalid || !mine) {
           x = -INFINITY;
         } else if (PEN && q_out && sg == (uint32_t)kSegGuide) {
           const float dt = fabsf(qt - tss[j]);
@@ -125,8 +150,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   // and value tail_v
   float tail_w = 0.f;
   const float* tail_v = nullptr;
-  if (SPARSE && a.tail_lse) {
-    const int64_t tb = (int64_t)h * a.nqb + qblk;
+  if (SPARSE && a.tail_lse && !sink_map[my_map]) {
+    const int64_t tb = (int64_t)h * a.nqb + qrow / bs;
     const float lt = a.tail_lse[tb];
     if (lt != -INFINITY) {
       const float m_new = fmaxf(m, lt);
@@ -154,8 +179,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, bool SPARSE, bool PEN>
 hipError_t launch_f32_variant(const AttnArgs& a, hipStream_t s) {
-  const int nblk = SPARSE ? a.nqb : (a.nq + 63) / 64;
-  dim3 grid(nblk, a.H);
+  dim3 grid((a.nq + 63) / 64, a.H);
   attn_f32_kernel<D, SPARSE, PEN><<<grid, 64, 0, s>>>(a);
   return hipGetLastError();
 }

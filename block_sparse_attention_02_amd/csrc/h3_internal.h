@@ -7,11 +7,12 @@
 
 namespace h3 {
 
-constexpr int kTile = 64;         // key tile = routing block = 64 rows
+constexpr int kTile = 64;         // key tile of the attention kernels = 64 rows
 constexpr int kSegText = 0, kSegGuide = 1, kSegAudio = 2, kSegOutput = 3;
 constexpr int kSegInvalid = 255;  // marks key slots past the end of a tile
-// Largest sequence the router and the block-sparse kernels accept, in 64-row blocks
-// (896,000 rows); their per-workgroup tile bitmaps in LDS are sized for it.
+// Largest block count the router and the block-sparse kernels accept, at every block
+// size, and at most this many 64-row tiles (896,000 rows): the per-workgroup bitmaps
+// and the router's per-block scores live in LDS.
 constexpr int kMaxBlocks = 14000;
 constexpr int kBitmapWords = (kMaxBlocks + 31) / 32;
 
@@ -51,7 +52,9 @@ struct AttnArgs {
   int n_prot;
   const int32_t* tiles;     // [H][nqb][k_sel]
   int k_sel;
-  int nqb;
+  int nqb;                  // query blocks of the lists: ceil(nq / bs)
+  int bs;                   // rows per routing block: 32, 64 or 128
+  uint32_t sink_mask;       // bit s: query blocks holding a row of segment s attend all keys
   // optional tail key per query block (block-sparse with tail term), else null
   const float* tail_lse;    // [H][nqb] natural log
   const float* tail_v;      // [H][nqb][D]
@@ -81,17 +84,18 @@ struct RouterWs {
 struct TailArgs {
   float scale;         // attention scale applied to the pooled scores
   int n;               // rows of the sequence (counts of the ragged last tile)
+  int bs;              // rows per block
   const float* vbar;   // [H][nb][D] block means of v
   float* lse;          // [H][nb] natural-log logit of the tail key
   float* v;            // [H][nb][D] value of the tail key
 };
-size_t router_ws_bytes(int n, int H, int D, bool tail);
-RouterWs router_ws_carve(void* ws, int n, int H, int D, bool tail);
+size_t router_ws_bytes(int n, int H, int D, int bs, bool tail);
+RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail);
 int router_max_blocks();
 hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
-                         int D, const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
-                         int32_t* prot, int prot_cap, const RouterWs& w, float scale,
-                         float* tail_lse, float* tail_v, hipStream_t s);
+                         int D, int bs, const uint8_t* seg, int prefix, int k_sel,
+                         int32_t* tiles, int32_t* prot, int prot_cap, const RouterWs& w,
+                         float scale, float* tail_lse, float* tail_v, hipStream_t s);
 
 // LSE merge and accumulator finalisation.
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

@@ -6,8 +6,9 @@
 // "H3 sparse-attention breakpoints": the density is a fraction of the video KV tiles.
 //
 // Three kernels, all deterministic (no floating-point atomics):
-//   1. flags   : protected / video classification of the 64-row blocks and their
-//                ascending lists (one workgroup, ballot-based compaction);
+//   1. flags   : protected / video classification of the blocks (32, 64 or 128 rows,
+//                the same size for queries and keys) and their ascending lists (one
+//                workgroup, ballot-based compaction);
 //   2. pool    : per-block means of q and k, float32 sums in row order, one pass over
 //                q and k in HBM (memory bound);
 //   3. score+top-k: per head and group of query blocks, pooled scores against every
@@ -33,6 +34,7 @@ constexpr int kTopkWaves = 4;
 // ------------------------------------------------------------------ 1. flags
 __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __restrict__ seg,
                                                             int n, int prefix, int nb,
+                                                            int bs,
                                                             int32_t* __restrict__ prot,
                                                             int prot_cap,
                                                             int32_t* __restrict__ video,
@@ -50,8 +52,8 @@ __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __res
     const bool valid = b < nb;
     bool isp = false;
     if (valid) {
-      const int lo = b * kTile;
-      const int hi = min(n, lo + kTile);
+      const int lo = b * bs;
+      const int hi = min(n, lo + bs);
       isp = lo < prefix;
       for (int r = lo; r < hi && !isp; ++r) {
         const int s = seg[r];
@@ -83,12 +85,12 @@ __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __res
 }
 
 // ------------------------------------------------------------------ 2. pool
-// Thread = 8 consecutive (head, d) elements of a row; workgroup = one 64-row block.
+// Thread = 8 consecutive (head, d) elements of a row; workgroup = one block of bs rows.
 template <bool BF16, int D, bool TAIL>
 __global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict__ q,
                                                           const void* __restrict__ k,
                                                           const void* __restrict__ v, int n,
-                                                          int H, int nb,
+                                                          int H, int nb, int bs,
                                                           float* __restrict__ qbar,
                                                           float* __restrict__ kbar,
                                                           float* __restrict__ vbar) {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict
   const int e0 = (blockIdx.y * 128 + threadIdx.x) * 8;
   if (e0 >= H * D) return;
   const int h = e0 / D, d0 = e0 % D;
-  const int lo = b * kTile, hi = min(n, lo + kTile);
+  const int lo = b * bs, hi = min(n, lo + bs);
   const int64_t rs = (int64_t)H * D;
   float aq[8], ak[8], av[8];
 #pragma unroll
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       const float s = my_w[i];
       if (s != -INFINITY) {
         const int kb = video[i];
-        const float x = s * tail.scale + __logf((float)min(kTile, tail.n - kb * kTile));
+        const float x = s * tail.scale + __logf((float)min(tail.bs, tail.n - kb * tail.bs));
         my_w[i] = x;
         mx = fmaxf(mx, x);
       }
@@ -339,19 +341,35 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
   }
   __syncthreads();
-  constexpr int GROUPS = 256 / D;  // query blocks handled side by side
+  // weighted V means: thread (g, d) takes every GROUPS-th video tile for all QB query
+  // blocks at once (one vbar read serves QB products), then the groups are added
+  constexpr int GROUPS = 256 / D;
+  __shared__ float part[GROUPS > 1 ? (GROUPS - 1) * QB * D : 1];
   const int d = tid % D, g = tid / D;
-  for (int j0 = g; j0 < QB; j0 += GROUPS) {
-    float acc = 0.f;
-    const float* wj = sc + j0 * nv;
-    for (int i = 0; i < nv; ++i) {
-      const float wt = wj[i];
-      if (wt != 0.f) acc += wt * tail.vbar[((int64_t)h * nb + video[i]) * D + d];
-    }
-    const int qj = qb0 + j0;
-    if (qj < nb) {
-      const float sm = tsum[j0];
-      tail.v[((int64_t)h * nb + qj) * D + d] = sm > 0.f ? acc / sm : 0.f;
+  float acc[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) acc[j] = 0.f;
+  const float* vh = tail.vbar + (int64_t)h * nb * D + d;
+#pragma unroll 4
+  for (int i = g; i < nv; i += GROUPS) {
+    const float vb = vh[(int64_t)video[i] * D];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) acc[j] += sc[j * nv + i] * vb;
+  }
+  if (g > 0) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) part[((g - 1) * QB + j) * D + d] = acc[j];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      for (int gg = 1; gg < GROUPS; ++gg) acc[j] += part[((gg - 1) * QB + j) * D + d];
+      const int qj = qb0 + j;
+      if (qj < nb) {
+        const float sm = tsum[j];
+        tail.v[((int64_t)h * nb + qj) * D + d] = sm > 0.f ? acc[j] / sm : 0.f;
+      }
     }
   }
 }
@@ -360,14 +378,14 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t router_ws_bytes(int n, int H, int D, bool tail) {
-  const size_t nb = (size_t)((n + kTile - 1) / kTile);
+size_t router_ws_bytes(int n, int H, int D, int bs, bool tail) {
+  const size_t nb = (size_t)((n + bs - 1) / bs);
   const size_t means = align256(nb * H * D * sizeof(float));
   return (tail ? 3 : 2) * means + align256(nb * sizeof(int32_t)) + 256;
 }
 
-RouterWs router_ws_carve(void* ws, int n, int H, int D, bool tail) {
-  const size_t nb = (size_t)((n + kTile - 1) / kTile);
+RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
+  const size_t nb = (size_t)((n + bs - 1) / bs);
   const size_t means = align256(nb * H * D * sizeof(float));
   char* p = (char*)ws;
   RouterWs w;
@@ -395,15 +413,24 @@ void launch_topk(dim3 grid, size_t lds, hipStream_t s, const RouterWs& w, int nb
 
 template <int D, bool TAIL>
 void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, int n, int H,
-                      int nb, int k_sel, int32_t* tiles, const RouterWs& w, const TailArgs& ta,
-                      hipStream_t s) {
+                      int nb, int bs, int k_sel, int32_t* tiles, const RouterWs& w,
+                      const TailArgs& ta, hipStream_t s) {
   const int chunks = (H * D / 8 + 127) / 128;
   dim3 pgrid(nb, chunks);
   if (bf16)
-    router_pool_kernel<true, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, w.qbar, w.kbar, w.vbar);
+    router_pool_kernel<true, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, bs, w.qbar,
+                                                             w.kbar, w.vbar);
   else
-    router_pool_kernel<false, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, w.qbar, w.kbar, w.vbar);
-  const bool wide = (size_t)4 * nb * sizeof(float) <= 56 * 1024;
+    router_pool_kernel<false, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, bs, w.qbar,
+                                                              w.kbar, w.vbar);
+  // four query blocks per workgroup when their scores fit in this device's LDS next to
+  // the kernel's own arrays (about 12 KB)
+  int dev = 0, max_lds = 64 * 1024;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+          hipSuccess)
+    max_lds = 64 * 1024;
+  const bool wide = (size_t)4 * nb * sizeof(float) + 12 * 1024 <= (size_t)max_lds;
   const int qb = wide ? 4 : 1;
   dim3 tgrid((nb + qb - 1) / qb, H);
   const size_t lds = (size_t)qb * nb * sizeof(float);
@@ -414,21 +441,22 @@ void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, in
 }
 
 hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
-                         int D, const uint8_t* seg, int prefix, int k_sel, int32_t* tiles,
-                         int32_t* prot, int prot_cap, const RouterWs& w, float scale,
-                         float* tail_lse, float* tail_v, hipStream_t s) {
-  const int nb = (n + kTile - 1) / kTile;
-  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, prot, prot_cap, w.video, w.counts);
+                         int D, int bs, const uint8_t* seg, int prefix, int k_sel,
+                         int32_t* tiles, int32_t* prot, int prot_cap, const RouterWs& w,
+                         float scale, float* tail_lse, float* tail_v, hipStream_t s) {
+  const int nb = (n + bs - 1) / bs;
+  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, bs, prot, prot_cap, w.video,
+                                         w.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool tail = tail_lse != nullptr;
-  const TailArgs ta{scale, n, w.vbar, tail_lse, tail_v};
+  const TailArgs ta{scale, n, bs, w.vbar, tail_lse, tail_v};
   if (D == 128) {
-    if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
-    else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
+    if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
+    else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
   } else {
-    if (tail) launch_pool_topk<64, true>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
-    else launch_pool_topk<64, false>(q, k, v, bf16, n, H, nb, k_sel, tiles, w, ta, s);
+    if (tail) launch_pool_topk<64, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
+    else launch_pool_topk<64, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
   }
   return hipGetLastError();
 }

@@ -38,7 +38,7 @@ extern "C" {
 
 #define H3_OK            0
 #define H3_EINVAL       (-1)  /* null pointer, bad size, non-finite or out-of-range knob */
-#define H3_EUNSUPPORTED (-2)  /* dtype, head_dim not in {64,128}, block_size != 64 */
+#define H3_EUNSUPPORTED (-2)  /* dtype, head_dim not in {64,128}, block_size not in {32,64,128} */
 #define H3_ELAUNCH      (-3)  /* a kernel launch failed (hipGetLastError) */
 #define H3_EWORKSPACE   (-4)  /* workspace pointer null or smaller than required */
 
@@ -89,6 +89,14 @@ int attn_dense_tara(const void* q, const void* k, const void* v, int dtype,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Block size of the router and the block-sparse calls: 32, 64 or 128 rows
+ * ("H3 SLA Attention", inputs table, block_size: the number of rows that share
+ * one key selection). Query blocks and key blocks have the same size, and the
+ * same rules hold at each size. A sequence may have at most 14,000 blocks of
+ * that size and at most 896,000 rows.
+ */
+
+/*
  * Router plan (host only, no HIP call).
  * From "H3 SLA Attention" ("How it works", "The inputs that matter", inputs
  * table) and "H3 sparse-attention breakpoints" (the density is a fraction of
@@ -101,7 +109,7 @@ int attn_dense_tara(const void* q, const void* k, const void* v, int dtype,
  * seg_host: [n] host segment ids. Outputs may be NULL when not wanted.
  * Errors: H3_EINVAL (seg_host null, n <= 0, protected_prefix_len not in
  * [0, n], sparsity_ratio not in [0, 1) or non-finite); H3_EUNSUPPORTED
- * (block_size != 64).
+ * (block_size not in {32, 64, 128}).
  */
 int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, int block_size,
                      double sparsity_ratio, int* nb, int* n_video, int* n_prot, int* k_sel);
@@ -117,15 +125,15 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
  * kb only; the k_sel highest scores are kept (ties to the lower block index,
  * NaN last) and written in ascending block order. Every query block is
  * routed, text and audio blocks included.
- * tiles: device int32 [heads][ceil(n/64)][k_sel]; entries past the device's
- *        video-tile count are -1.
+ * tiles: device int32 [heads][nb][k_sel], nb = ceil(n / block_size); entries
+ *        past the device's video-tile count are -1.
  * prot:  device int32 [n_prot] ascending protected block indices; n_prot is the
  *        count from attn_router_plan on the same seg, and at most n_prot entries
  *        are written.
  * Workspace: attn_block_router_workspace(n, heads, head_dim, block_size).
  * Errors: as attn_router_plan, plus H3_EINVAL for null q/k/seg, null tiles
- * (k_sel > 0), null prot (n_prot > 0), k_sel < 0, k_sel > ceil(n/64) or
- * n_prot < 0; H3_EUNSUPPORTED for dtype/head_dim or more than 14,000 blocks;
+ * (k_sel > 0), null prot (n_prot > 0), k_sel < 0, k_sel > nb or n_prot < 0;
+ * H3_EUNSUPPORTED for dtype/head_dim/block_size or more than 14,000 blocks;
  * H3_EWORKSPACE; H3_ELAUNCH.
  */
 size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size);
@@ -139,14 +147,17 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
  * From "H3 SLA Attention", "How it works" and inputs table: query block qb of
  * head h attends the keys of the set of blocks formed by its protected blocks
  * prot[0..n_prot) and its routed blocks tiles[h][qb][0..k_sel), and nothing
- * else (a hard zero, no tail term). Entries outside [0, ceil(n/64)) are
- * skipped and a block listed more than once counts once. Inside those tiles the
+ * else (a hard zero, no tail term). Blocks are block_size rows; tiles is
+ * [heads][ceil(n / block_size)][k_sel]. Entries outside [0, ceil(n /
+ * block_size)) are skipped and a block listed more than once counts once.
+ * Inside those tiles the
  * score is the dense TARA score of attn_dense_tara, so the penalty applies to
  * routed guide tiles of output-video queries when strength > 0 and cap > 0.
  * Workspace: attn_block_sparse_workspace(n, heads, head_dim, dtype) bytes.
  * Errors: as attn_dense_tara, plus H3_EINVAL for k_sel < 0, n_prot < 0,
  * n_prot + k_sel == 0, null tiles (k_sel > 0) or prot (n_prot > 0);
- * H3_EUNSUPPORTED for block_size != 64 or more than 14,000 blocks.
+ * H3_EUNSUPPORTED for block_size not in {32, 64, 128}, more than 14,000 blocks
+ * or more than 896,000 rows.
  */
 size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype);
 int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,
@@ -172,8 +183,8 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,
  * Same routing outputs and rules as attn_block_router, plus:
  * v:        device [n][heads][head_dim] values (dtype as q/k);
  * scale:    the attention scale of the sparse call (> 0);
- * tail_lse: device float32 [heads][ceil(n/64)]; tail_v: device float32
- *           [heads][ceil(n/64)][head_dim].
+ * tail_lse: device float32 [heads][nb]; tail_v: device float32
+ *           [heads][nb][head_dim], nb = ceil(n / block_size).
  * Workspace: attn_block_router_tail_workspace(n, heads, head_dim, block_size).
  * Errors: as attn_block_router, plus H3_EINVAL for null v/tail_lse/tail_v or a
  * non-finite or non-positive scale.
@@ -202,6 +213,32 @@ int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtyp
                            const float* tail_lse, const float* tail_v,
                            void* o, int o_dtype, float* lse,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention with sink query blocks.
+ * From "Per-layer attention config LoRAs", section "Experimental: audio/text
+ * protection": the audio queries are kept fully exact (sink_queries = audio).
+ * attn_block_sparse, where a query block holding any row whose segment id s
+ * has bit s set in sink_segments attends every key of the sequence (its list
+ * is not read, and it takes no tail term: nothing is left out). The whole
+ * block is dense, including its non-sink rows at a segment boundary.
+ * sink_segments: bit mask over segment ids 0..3; 1 << H3_SEG_AUDIO gives the
+ *           audio sink queries, 0 gives attn_block_sparse.
+ * tail_lse, tail_v: both NULL (hard zero for left-out tiles) or both set (the
+ *           tail term of attn_block_sparse_tail for the other blocks).
+ * Workspace as attn_block_sparse.
+ * Errors: as attn_block_sparse, plus H3_EINVAL for sink_segments bits above
+ * bit 3 or only one of tail_lse and tail_v set.
+ */
+int attn_block_sparse_sinks(const void* q, const void* k, const void* v, int dtype,
+                            int n, int heads, int head_dim,
+                            const uint8_t* seg, const float* t,
+                            float strength, float window, float falloff, float cap, float scale,
+                            int block_size, const int32_t* tiles, int k_sel,
+                            const int32_t* prot, int n_prot,
+                            const float* tail_lse, const float* tail_v, unsigned sink_segments,
+                            void* o, int o_dtype, float* lse,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Stable LSE merge of one partition result into an accumulator, in place.

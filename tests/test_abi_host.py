@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(api.EXPORTS)
     L = api.lib()
     for n in names:
@@ -54,12 +54,13 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 # ----------------------------------------------------------- router plan (host)
 
+@pytest.mark.parametrize("bs", [32, 64, 128])
 @pytest.mark.parametrize("wl", [W.MID_SPARSE, W.FULL_SPARSE])
-def test_router_plan_matches_oracle(wl):
+def test_router_plan_matches_oracle(wl, bs):
     seg, _ = W.layout(wl)
     for s in (0.0,) + tuple(wl.sparsities) + (0.3, 0.999):
-        got = api.router_plan(seg, wl.protected_prefix_len, s)
-        nb, prot, vid, k = oracle.router_plan(seg, wl.protected_prefix_len, 64, s)
+        got = api.router_plan(seg, wl.protected_prefix_len, s, block_size=bs)
+        nb, prot, vid, k = oracle.router_plan(seg, wl.protected_prefix_len, bs, s)
         assert got == {"nb": nb, "n_video": len(vid), "n_prot": len(prot), "k_sel": k}
 
 
@@ -70,8 +71,9 @@ def test_router_plan_random_layouts_match_oracle():
         seg = rng.choice([0, 1, 2, 3], size=n, p=[0.05, 0.45, 0.05, 0.45]).astype(np.uint8)
         pre = int(rng.integers(0, n + 1))
         s = float(rng.choice([0.0, 0.5, 0.85, 0.9, 0.95, 0.999]))
-        got = api.router_plan(seg, pre, s)
-        nb, prot, vid, k = oracle.router_plan(seg, pre, 64, s)
+        bs = int(rng.choice([32, 64, 128]))
+        got = api.router_plan(seg, pre, s, block_size=bs)
+        nb, prot, vid, k = oracle.router_plan(seg, pre, bs, s)
         assert got == {"nb": nb, "n_video": len(vid), "n_prot": len(prot), "k_sel": k}
 
 
@@ -86,8 +88,10 @@ def test_router_plan_errors():
     assert L.attn_router_plan(ptr, 100, 0, 64, 1.0, N0, N0, N0, N0) == api.H3_EINVAL
     assert L.attn_router_plan(ptr, 100, 0, 64, -0.1, N0, N0, N0, N0) == api.H3_EINVAL
     assert L.attn_router_plan(ptr, 100, 0, 64, float("nan"), N0, N0, N0, N0) == api.H3_EINVAL
-    assert L.attn_router_plan(ptr, 100, 0, 128, 0.5, N0, N0, N0, N0) == api.H3_EUNSUPPORTED
-    assert L.attn_router_plan(ptr, 100, 0, 64, 0.5, N0, N0, N0, N0) == api.H3_OK
+    for bs in (0, 16, 48, 256):
+        assert L.attn_router_plan(ptr, 100, 0, bs, 0.5, N0, N0, N0, N0) == api.H3_EUNSUPPORTED
+    for bs in (32, 64, 128):
+        assert L.attn_router_plan(ptr, 100, 0, bs, 0.5, N0, N0, N0, N0) == api.H3_OK
 
 
 # ----------------------------------------------------------- argument checks
@@ -132,9 +136,12 @@ def test_workspace_sizes():
     assert L.attn_dense_tara_workspace(100, 3, 128, 0) == 0
     assert L.attn_dense_tara_workspace(100, 3, 96, 1) == 0
     assert L.attn_block_sparse_workspace(129, 2, 64, 1) == _a256(2 * 64 * 192 * 2) + _a256(3 * 16)
-    nb = (31552 + 63) // 64
-    assert L.attn_block_router_workspace(31552, 24, 128, 64) >= 2 * nb * 24 * 128 * 4
-    assert L.attn_block_router_workspace(31552, 24, 128, 32) == 0
+    for bs in (32, 64, 128):
+        nb = (31552 + bs - 1) // bs
+        # two float32 means per (head, block, d), the video-block list and the counts
+        assert (L.attn_block_router_workspace(31552, 24, 128, bs)
+                == 2 * _a256(nb * 24 * 128 * 4) + _a256(nb * 4) + 256)
+    assert L.attn_block_router_workspace(31552, 24, 128, 16) == 0
 
 
 def sparse(**kw):
@@ -153,8 +160,9 @@ def sparse(**kw):
     ({"q": None}, -1), ({"seg": None}, -1), ({"t": None}, -1), ({"n": 0}, -1),
     ({"ksel": -1}, -1), ({"nprot": -1}, -1), ({"ksel": 0, "nprot": 0}, -1),
     ({"tiles": None}, -1), ({"prot": None}, -1), ({"falloff": 0.0}, -1),
-    ({"bs": 128}, -2), ({"bs": 32}, -2), ({"d": 80}, -2), ({"dtype": 3}, -2),
-    ({}, -4),
+    ({"bs": 16}, -2), ({"bs": 256}, -2), ({"d": 80}, -2), ({"dtype": 3}, -2),
+    ({"bs": 32, "n": 14001 * 32}, -2), ({"bs": 128, "n": 14000 * 64 + 1}, -2),
+    ({}, -4), ({"bs": 32}, -4), ({"bs": 128}, -4), ({"bs": 32, "n": 14000 * 32}, -4),
 ])
 def test_sparse_argument_checks(kw, code):
     assert sparse(**kw) == code
@@ -173,8 +181,9 @@ def router(**kw):
     ({"q": None}, -1), ({"k": None}, -1), ({"seg": None}, -1), ({"n": 0}, -1),
     ({"heads": -1}, -1), ({"pre": -1}, -1), ({"pre": 641}, -1), ({"ksel": -1}, -1),
     ({"ksel": 11}, -1), ({"tiles": None}, -1), ({"prot": None}, -1), ({"nprot": -2}, -1),
-    ({"bs": 128}, -2), ({"d": 32}, -2), ({"dtype": 7}, -2), ({"n": 14001 * 64}, -2),
-    ({}, -4), ({"ws": P, "wsb": 8}, -4),
+    ({"bs": 16}, -2), ({"d": 32}, -2), ({"dtype": 7}, -2), ({"n": 14001 * 64}, -2),
+    ({"bs": 32, "n": 14001 * 32}, -2), ({"bs": 128, "n": 14000 * 64 + 1}, -2),
+    ({}, -4), ({"ws": P, "wsb": 8}, -4), ({"bs": 32}, -4), ({"bs": 128}, -4),
 ])
 def test_router_argument_checks(kw, code):
     assert router(**kw) == code
@@ -235,3 +244,21 @@ def test_tail_entry_points_reject_bad_arguments():
     assert L.attn_block_sparse_tail(*sp, None, P, P, 1, P, P, 1 << 30, None) == -1
     assert L.attn_block_sparse_tail(*sp, P, None, P, 1, P, P, 1 << 30, None) == -1
     assert L.attn_block_sparse_tail(*sp, P, P, P, 1, P, None, 0, None) == -4
+
+
+def test_sink_entry_point_rejects_bad_arguments():
+    """Sink query blocks: the segment mask holds segment ids 0..3 only, and the tail
+    pointers come both or neither; checked before any HIP call."""
+    L = api.lib()
+    P = ctypes.c_void_p(16)
+    sp = [P, P, P, 1, 1000, 2, 64, P, P, 2.0, 0.2, 0.25, 6.0, 0.125, 64, P, 4, P, 1]
+    tail = [P, P]
+    assert L.attn_block_sparse_sinks(*sp, *tail, 1 << 2, P, 1, P, None, 0, None) == -4
+    assert L.attn_block_sparse_sinks(*sp, None, None, 1 << 2, P, 1, P, None, 0, None) == -4
+    assert L.attn_block_sparse_sinks(*sp, None, None, 0, P, 1, P, None, 0, None) == -4
+    assert L.attn_block_sparse_sinks(*sp, *tail, 1 << 4, P, 1, P, None, 0, None) == -1
+    assert L.attn_block_sparse_sinks(*sp, P, None, 1 << 2, P, 1, P, None, 0, None) == -1
+    assert L.attn_block_sparse_sinks(*sp, None, P, 1 << 2, P, 1, P, None, 0, None) == -1
+    bad = list(sp)
+    bad[14] = 96
+    assert L.attn_block_sparse_sinks(*bad, *tail, 1 << 2, P, 1, P, None, 0, None) == -2

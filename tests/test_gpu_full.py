@@ -178,3 +178,49 @@ def test_full_sparse_with_tail_sampled(full):
         lrf.append(lb)
     compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
             "full sparse tail s=0.9")
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_full_block_sizes_with_audio_sinks_sampled(full, bs):
+    """Full scale, s = 0.90, blocks of 32 or 128 rows, TARA on routed guide tiles, audio
+    sink query blocks dense: router lists of the sampled heads bit-exact, outputs of
+    sampled blocks (segment boundaries, the audio span, the ragged tail) against the
+    oracle."""
+    wl, seg, t, dev, host, host32 = full
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.90, block_size=bs)
+    print(f"router + sparse + audio sinks bs={bs} k={plan['k_sel']}", flush=True)
+    tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
+                                        plan["k_sel"], plan["n_prot"], block_size=bs)
+    o, lse = api.attn_block_sparse_sinks(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"],
+                                         tiles, prot, 1 << W.SEG_AUDIO, None, None, *wl.tara,
+                                         scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    tl = tiles.cpu().numpy()[HEADS]
+    pr = prot.cpu().numpy()
+    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, bs, 0.90)
+    assert np.array_equal(pr, prot_ref)
+    for j in range(len(HEADS)):
+        ref = oracle.route_head(host32["q"][:, j], host32["k"][:, j], seg,
+                                wl.protected_prefix_len, bs, plan["k_sel"])
+        mism = int(np.sum(np.any(tl[j] != ref, axis=1)))
+        print(f"bs={bs} head {HEADS[j]}: {mism} mismatching tile lists of {plan['nb']}",
+              flush=True)
+        assert mism == 0
+    nb = plan["nb"]
+    # blocks holding rows 0, 7258/7259 (text/guide), 61570/61571 (guide/audio), 62000
+    # (audio), 62570/62571 (audio/output), 90000 and the last row
+    blocks = sorted({r // bs for r in (0, 7258, 7259, 61570, 61571, 62000, 62570, 62571,
+                                       90000, wl.n - 1)})
+    ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, bs, pr,
+                              tl, heads=range(len(HEADS)), qblocks=blocks,
+                              sink_segments=(W.SEG_AUDIO,))
+    og, lg, orf, lrf = [], [], [], []
+    for (j, qb), (ob, lb) in ref.items():
+        lo, hi = qb * bs, min(wl.n, qb * bs + bs)
+        og.append(o[lo:hi, HEADS[j]])
+        lg.append(lse[lo:hi, HEADS[j]])
+        orf.append(ob)
+        lrf.append(lb)
+    assert blocks[-1] == nb - 1
+    compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
+            f"full sparse bs={bs} audio sinks")

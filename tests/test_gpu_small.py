@@ -124,10 +124,10 @@ def test_dense_is_deterministic():
 
 # ------------------------------------------------------------------- router
 
-def _route_oracle(wl, q, k, seg, k_sel, heads):
+def _route_oracle(wl, q, k, seg, k_sel, heads, bs=64):
     return np.stack([oracle.route_head(W.to_float32(q[:, j], wl.dtype),
                                        W.to_float32(k[:, j], wl.dtype), seg,
-                                       wl.protected_prefix_len, 64, k_sel) for j in heads])
+                                       wl.protected_prefix_len, bs, k_sel) for j in heads])
 
 
 def test_router_mid_bit_exact():
@@ -289,12 +289,12 @@ def test_sparse_hand_built_lists(d, dtype):
 
 # ------------------------------------------------------------------- tail term
 
-def _tails_oracle(wl, q, k, v, seg, tiles, heads):
+def _tails_oracle(wl, q, k, v, seg, tiles, heads, bs=64):
     """oracle.tail_terms for the given heads: {j: (lse [nqb], v [nqb, d])}."""
     out = {}
     for j, h in enumerate(heads):
         out[j] = oracle.tail_terms(W.to_float32(q[:, h], wl.dtype), W.to_float32(k[:, h], wl.dtype),
-                                   f64(v[:, h], wl.dtype), seg, wl.protected_prefix_len, 64,
+                                   f64(v[:, h], wl.dtype), seg, wl.protected_prefix_len, bs,
                                    tiles[h], wl.scale)
     return out
 

@@ -1,0 +1,205 @@
+"""GPU parity of the routing variants: block sizes 32 and 128 (router lists
+bit-exact, tail terms, sparse outputs) and audio sink query blocks, against the
+float64 oracle at sizes it finishes in seconds ("H3 SLA Attention", inputs table,
+block_size; "Per-layer attention config LoRAs", section "Experimental: audio/text
+protection")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_02_amd import api, workloads as W
+from gpu_common import compare, f64, layout_device, to_device
+from test_gpu_small import _route_oracle, _tails_oracle
+
+pytestmark = pytest.mark.gpu
+
+AUDIO_SINK = 1 << W.SEG_AUDIO
+
+
+def _pen_case(dtype, heads=3, seed=120, tail_rows=0):
+    d = 128 if dtype == "bf16" else 64
+    spans = [W.Span(W.SEG_TEXT, 100), W.Span(W.SEG_GUIDE, 8 * 130, 8),
+             W.Span(W.SEG_AUDIO, 60), W.Span(W.SEG_OUTPUT, 8 * 130, 8)]
+    if tail_rows:
+        spans.append(W.Span(W.SEG_TEXT, tail_rows))
+    return W.custom(f"var_{dtype}_{seed}", spans, heads=heads, head_dim=d, dtype=dtype,
+                    seed_index=seed, frame_weight=0.7, protected_prefix_len=100)
+
+
+def _assemble(ref, n, heads, d, bs):
+    o_ref = np.zeros((n, heads, d))
+    l_ref = np.zeros((n, heads))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * bs:qb * bs + len(ob), h] = ob
+        l_ref[qb * bs:qb * bs + len(ob), h] = lb
+    return o_ref, l_ref
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_router_block_sizes_bit_exact(bs):
+    """31,552 rows, 24 heads, s = 0.85, blocks of 32 or 128 rows: protected list and
+    every tile list of six heads bit-exact."""
+    wl = W.MID_SPARSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.85, block_size=bs)
+    print(f"case router bs={bs} plan={plan}", flush=True)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, wl.protected_prefix_len, plan["k_sel"],
+                                        plan["n_prot"], block_size=bs)
+    torch.cuda.synchronize()
+    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, bs, 0.85)
+    assert np.array_equal(prot.cpu().numpy(), prot_ref)
+    heads = [0, 5, 11, 17, 22, 23]
+    ref = _route_oracle(wl, q, k, seg, plan["k_sel"], heads, bs=bs)
+    got = tiles.cpu().numpy()[heads]
+    mism = int(np.sum(np.any(got != ref, axis=2)))
+    print(f"router bs={bs} mismatching lists: {mism} of {got.shape[0] * got.shape[1]}")
+    assert mism == 0
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_router_tail_terms_block_sizes(bs):
+    """Tail logits and values at block sizes 32 and 128 against the oracle."""
+    wl = W.MID_SPARSE
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.85, block_size=bs)
+    print(f"case router tail bs={bs}", flush=True)
+    tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, wl.protected_prefix_len,
+                                                     plan["k_sel"], plan["n_prot"],
+                                                     scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    heads = [0, 23]
+    ref = _tails_oracle(wl, q, k, v, seg, tiles.cpu().numpy(), heads, bs=bs)
+    tl, tv = tl.cpu().numpy(), tv.cpu().numpy()
+    for j, h in enumerate(heads):
+        l_ref, v_ref = ref[j]
+        assert np.array_equal(np.isneginf(tl[h]), np.isneginf(l_ref))
+        fin = np.isfinite(l_ref)
+        el = float(np.max(np.abs(tl[h][fin] - l_ref[fin])))
+        ev = float(np.max(np.abs(tv[h] - v_ref)))
+        print(f"[tail terms bs={bs} head {h}] lse err {el:.2e} v err {ev:.2e}", flush=True)
+        assert el < 1e-3 and ev < 1e-3
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+@pytest.mark.parametrize("dtype,sparsity,tail", [("bf16", 0.5, False), ("bf16", 0.9, False),
+                                                 ("bf16", 0.8, True), ("f32", 0.7, False),
+                                                 ("f32", 0.9, True)])
+def test_sparse_block_sizes_small(bs, dtype, sparsity, tail):
+    """Router + sparse attention (TARA penalty on routed guide tiles, optional tail) at
+    block sizes 32 and 128; every output row against the oracle. 19 trailing text rows
+    leave ragged last blocks."""
+    wl = _pen_case(dtype, tail_rows=19)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    plan = api.router_plan(seg, 100, sparsity, block_size=bs)
+    print(f"case sparse bs={bs} {dtype} s={sparsity} tail={tail} plan={plan}", flush=True)
+    if tail:
+        tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, 100, plan["k_sel"],
+                                                         plan["n_prot"], scale=wl.scale,
+                                                         block_size=bs)
+        o, lse = api.attn_block_sparse_tail(qd, kd, vd, seg_d, t_d, tiles, prot, tl, tv,
+                                            *wl.tara, scale=wl.scale, block_size=bs)
+    else:
+        tiles, prot = api.attn_block_router(qd, kd, seg_d, 100, plan["k_sel"], plan["n_prot"],
+                                            block_size=bs)
+        o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
+                                       scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    tiles_np = tiles.cpu().numpy()
+    assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(3), bs=bs))
+    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3), bs=bs) if tail else None
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails)
+    o_ref, l_ref = _assemble(ref, wl.n, 3, wl.head_dim, bs)
+    compare(o, lse, o_ref, l_ref, dtype, f"sparse bs={bs} {dtype} s={sparsity} tail={tail}")
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sparse_block_sizes_hand_built_lists(bs, dtype):
+    """Random lists per block with repeats, -1 and out-of-range entries, a protected list
+    out of order: at block size 32 neighbouring 32-row blocks pick different halves of
+    the same 64-key tiles."""
+    wl = _pen_case(dtype, heads=2, seed=121, tail_rows=45)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    nb = (wl.n + bs - 1) // bs
+    rng = np.random.default_rng(bs)
+    k_sel = 9
+    tl = rng.integers(0, nb, size=(2, nb, k_sel)).astype(np.int32)
+    tl[:, :, 0] = tl[:, :, 1]
+    tl[:, ::3, 2] = -1
+    tl[:, ::5, 3] = nb + 4
+    prot = np.array([3, 0, nb - 1], dtype=np.int32)
+    print(f"case hand lists bs={bs} {dtype} n={wl.n}", flush=True)
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, torch.from_numpy(tl).cuda(),
+                                   torch.from_numpy(prot).cuda(), *wl.tara, scale=wl.scale,
+                                   block_size=bs)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, bs, prot, tl)
+    o_ref, l_ref = _assemble(ref, wl.n, 2, wl.head_dim, bs)
+    compare(o, lse, o_ref, l_ref, dtype, f"hand lists bs={bs} {dtype}")
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+@pytest.mark.parametrize("dtype,tail", [("bf16", False), ("bf16", True), ("f32", True)])
+def test_sparse_audio_sink_blocks(bs, dtype, tail):
+    """Query blocks holding audio rows attend every key (and take no tail term); the
+    others are routed as usual. Every output row against the oracle."""
+    wl = _pen_case(dtype, seed=122, tail_rows=7)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    plan = api.router_plan(seg, 100, 0.85, block_size=bs)
+    print(f"case sinks bs={bs} {dtype} tail={tail}", flush=True)
+    if tail:
+        tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, 100, plan["k_sel"],
+                                                         plan["n_prot"], scale=wl.scale,
+                                                         block_size=bs)
+    else:
+        tiles, prot = api.attn_block_router(qd, kd, seg_d, 100, plan["k_sel"], plan["n_prot"],
+                                            block_size=bs)
+        tl = tv = None
+    o, lse = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, AUDIO_SINK, tl, tv,
+                                         *wl.tara, scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    tiles_np = tiles.cpu().numpy()
+    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3), bs=bs) if tail else None
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails,
+                              sink_segments=(W.SEG_AUDIO,))
+    o_ref, l_ref = _assemble(ref, wl.n, 3, wl.head_dim, bs)
+    compare(o, lse, o_ref, l_ref, dtype, f"sinks bs={bs} {dtype} tail={tail}")
+    # the sink rows are the dense result
+    o_d, l_d = oracle.dense_tara(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, seg, t,
+                                 wl.tara, wl.scale)
+    rows = np.concatenate([np.arange(b * bs, min(wl.n, b * bs + bs)) for b in range(plan["nb"])
+                           if oracle.is_sink_block(seg, bs, b, (W.SEG_AUDIO,))])
+    compare(o[rows], lse[rows], o_d[rows], l_d[rows], dtype, f"sink rows dense bs={bs}")
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_sparse_every_tile_equals_dense_block_sizes(bs):
+    """Sparsity 0 at block sizes 32 and 128 reproduces dense TARA."""
+    wl = _pen_case("bf16", heads=2, seed=123, tail_rows=33)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, 100, 0.0, block_size=bs)
+    print(f"case s=0 bs={bs}", flush=True)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, 100, plan["k_sel"], plan["n_prot"],
+                                        block_size=bs)
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
+                                   scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense_tara(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, seg,
+                                     t, wl.tara, wl.scale)
+    compare(o, lse, o_ref, l_ref, "bf16", f"sparse s=0 bs={bs}")
