@@ -383,6 +383,55 @@ def main():
             "speedup_vs_dense": (d["ms"] / tot) if d else None}}
         print("# tail term done", file=sys.stderr, flush=True)
 
+        # routing variants at the benchmark sparsity: blocks of 32 and 128 rows, and audio
+        # sink query blocks (dense) at 64
+        def time_pair(route, attend):
+            rt, st = [], []
+            for rep in range(4):
+                a = ev()
+                route()
+                b = ev()
+                attend()
+                c = ev()
+                torch.cuda.synchronize()
+                if rep:
+                    rt.append(a.elapsed_time(b))
+                    st.append(b.elapsed_time(c))
+            r_ms, s_ms = float(np.median(rt)), float(np.median(st))
+            return {"router_ms": r_ms, "sparse_ms": s_ms, "ms": r_ms + s_ms,
+                    "speedup_vs_dense": (d["ms"] / (r_ms + s_ms)) if d else None}
+
+        for bsz in (32, 128):
+            pv = api.router_plan(seg, wl.protected_prefix_len, args.sparsity, block_size=bsz)
+            tv_, pr_ = api.attn_block_router(qd, kd, segd, wl.protected_prefix_len, pv["k_sel"],
+                                             pv["n_prot"], block_size=bsz)
+            ws_v = torch.empty(api.router_workspace_bytes(N, H, D, bsz), dtype=torch.uint8,
+                               device="cuda")
+            row = time_pair(
+                lambda: api.attn_block_router(qd, kd, segd, wl.protected_prefix_len,
+                                              pv["k_sel"], pv["n_prot"], block_size=bsz,
+                                              tiles=tv_, prot=pr_, ws=ws_v),
+                lambda: api.attn_block_sparse(qd, kd, vd, segd, td, tv_, pr_, *tara,
+                                              scale=scale, block_size=bsz, o=o_sparse,
+                                              lse=l_sparse, ws=ws_dense))
+            row.update({"sparsity": args.sparsity, "k_sel": pv["k_sel"],
+                        "kept_frac": (pv["n_prot"] + pv["k_sel"]) / pv["nb"]})
+            next_rows[f"block_size_{bsz}"] = row
+            del tv_, pr_, ws_v
+        row = time_pair(
+            lambda: api.attn_block_router(qd, kd, segd, wl.protected_prefix_len, k_sel, n_prot,
+                                          tiles=tiles, prot=prot, ws=ws_router),
+            lambda: api.attn_block_sparse_sinks(qd, kd, vd, segd, td, tiles, prot,
+                                                1 << W.SEG_AUDIO, None, None, *tara,
+                                                scale=scale, o=o_sparse, lse=l_sparse,
+                                                ws=ws_dense))
+        row.update({"sparsity": args.sparsity, "block_size": 64,
+                    "sink_query_blocks_per_head": int(sum(
+                        1 for b in range(nb)
+                        if np.any(seg[b * 64:(b + 1) * 64] == W.SEG_AUDIO)))})
+        next_rows["audio_sink_queries"] = row
+        print("# routing variants done", file=sys.stderr, flush=True)
+
     roofline = None
     if d:
         traffic = None
