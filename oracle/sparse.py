@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .quant import int8_roundtrip
 from .router import block_means_fp32, pooled_scores_fp32, router_plan
 from .tara import tara_bias, _softmax_rows
 
@@ -116,13 +117,14 @@ def block_sparse_block(q_h, k_h, v_h, seg, t, params, scale, block_size, prot, t
 
 
 def block_sparse(q, k, v, seg, t, params, scale, block_size, prot, tiles, heads=None,
-                 qblocks=None, tails=None, sink_segments=()):
+                 qblocks=None, tails=None, sink_segments=(), int8_qk=False):
     """Block-sparse outputs for the selected heads and query blocks.
 
     q, k, v: [n, H, d] float64; tiles: [H, nqb, k_sel]; tails: optional
     {h: (L_tail [nqb], v_tail [nqb, d])}; sink_segments: segment ids whose query
-    blocks attend densely. Returns {(h, qb): (o_rows, lse_rows)} for every
-    requested pair.
+    blocks attend densely; int8_qk: scores from the per-token int8 images of q and
+    k (oracle.quant; q and k must hold float32 values). Returns {(h, qb): (o_rows,
+    lse_rows)} for every requested pair.
     """
     n, H, d = q.shape
     nqb = (n + block_size - 1) // block_size
@@ -132,6 +134,8 @@ def block_sparse(q, k, v, seg, t, params, scale, block_size, prot, tiles, heads=
     for h in heads:
         qh = np.ascontiguousarray(q[:, h, :])
         kh = np.ascontiguousarray(k[:, h, :])
+        if int8_qk:
+            qh, kh = int8_roundtrip(qh), int8_roundtrip(kh)
         vh = np.ascontiguousarray(v[:, h, :])
         for qb in qblocks:
             tail = None if tails is None else (tails[h][0][qb], tails[h][1][qb])

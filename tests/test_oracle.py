@@ -725,3 +725,109 @@ def test_sink_query_blocks_attend_every_key(bs):
             assert np.max(np.abs(got[1] - l_d[lo:hi, 0])) < 1e-12
         else:
             assert np.array_equal(got[0], plain[0]) and np.array_equal(got[1], plain[1])
+
+
+# -------------------------------------------------------------- int8 QK
+
+def _quant_scalar(row):
+    """One row by scalar float32 operations: amax, s = amax / 127, rint(x / s) clamped."""
+    amax = np.float32(0.0)
+    for x in row:
+        amax = max(amax, np.float32(abs(np.float32(x))))
+    s = np.float32(amax / np.float32(127.0))
+    if s == 0:
+        return [0] * len(row), np.float32(0.0)
+    out = []
+    for x in row:
+        r = np.float32(np.float32(x) / s)
+        f = math.floor(float(r))
+        frac = float(r) - f
+        n = f + 1 if frac > 0.5 or (frac == 0.5 and f % 2 == 1) else f   # half to even
+        out.append(max(-127, min(127, int(n))))
+    return out, s
+
+
+def test_int8_quantization_brute_force_and_bounds():
+    """Per-token int8 ("H3 SLA Attention", inputs table, use_int8_qk): scalar float32
+    steps reproduce the vector form bit for bit; the largest element maps to +-127; every
+    element is within half a step of its dequantized value; a zero row stays zero."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 30, (40, 1))).astype(np.float32)
+    x[3] = 0.0
+    x[5, :] = np.float32(0.5)                # ties at x / s = 127 exactly
+    x[6, ::2] = np.float32(63.5) * np.float32(2.0 ** -6)
+    x[6, 1::2] = np.float32(127.0) * np.float32(2.0 ** -6)   # ties at 63.5: half to even
+    x8, s = oracle.quantize_int8(x)
+    for i in range(x.shape[0]):
+        ref, sr = _quant_scalar(x[i])
+        assert s[i] == sr and list(x8[i]) == ref, i
+    live = s > 0
+    assert np.all(np.max(np.abs(x8[live].astype(int)), axis=1) == 127)
+    xq = oracle.dequantize_int8(x8, s)
+    assert np.all(np.abs(xq - x) <= s[:, None].astype(np.float64) * (0.5 + 1e-6))
+    assert np.all(x8[3] == 0) and s[3] == 0
+    assert list(x8[6, :4]) == [64, 127, 64, 127]
+
+
+def test_int8_dot_identity():
+    """The integer product with the two scales equals the dot product of the dequantized
+    vectors (the GPU takes the former, the oracle's attention the latter)."""
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((20, 128)).astype(np.float32)
+    k = (rng.standard_normal((30, 128)) * 3).astype(np.float32)
+    q8, sq = oracle.quantize_int8(q)
+    k8, sk = oracle.quantize_int8(k)
+    ints = q8.astype(np.int64) @ k8.astype(np.int64).T
+    lhs = ints * sq[:, None].astype(np.float64) * sk[None, :].astype(np.float64)
+    rhs = oracle.dequantize_int8(q8, sq) @ oracle.dequantize_int8(k8, sk).T
+    assert np.max(np.abs(lhs - rhs) / (np.abs(rhs) + 1e-30)) < 1e-12
+
+
+def test_int8_exact_inputs_reproduce_plain_sparse():
+    """Inputs that are already int8 images (x = n * 2^-e with some |n| = 127) quantize
+    exactly, so the int8 path equals the plain block-sparse result."""
+    wl, seg, t, q, k, v = _sparse_case(seed=320)
+    rng = np.random.default_rng(23)
+    n, H, d = q.shape
+    def int8_like(shape):
+        m = rng.integers(-127, 128, size=shape).astype(np.float64)
+        m[..., 0] = 127.0
+        e = rng.integers(3, 9, size=shape[:-1])[..., None]
+        return (m * 2.0 ** -e).astype(np.float32)
+    q = int8_like((n, H, d))
+    k = int8_like((n, H, d))
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    assert np.array_equal(oracle.int8_roundtrip(q[:, 0]), q64[:, 0])
+    nb, prot, vid, kk = oracle.router_plan(seg, 40, 16, 0.7)
+    tiles = np.stack([np.sort(rng.choice(vid, kk, replace=False)).reshape(1, -1).repeat(
+        (n + 15) // 16, 0) for _ in range(H)])
+    a = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 16, prot, tiles)
+    b = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 16, prot, tiles,
+                            int8_qk=True)
+    for key in a:
+        assert np.array_equal(a[key][0], b[key][0]) and np.array_equal(a[key][1], b[key][1])
+
+
+def test_int8_sparse_brute_force_tiny():
+    """The int8 path is the plain score rule on the dequantized q and k (scalar loops),
+    and it differs from the unquantized result (the quantization is not a no-op)."""
+    wl, seg, t, q, k, v = _sparse_case(seed=321)
+    n = wl.n
+    prot = np.array([0, 2])
+    tiles = np.array([[[5, 9], [1, 30]], [[3, 4], [7, 8]]])
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    got = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 16, prot, tiles,
+                              qblocks=[0, 1], int8_qk=True)
+    plain = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 16, prot, tiles,
+                                qblocks=[0, 1])
+    for h in range(2):
+        qd = oracle.int8_roundtrip(q[:, h])
+        kd = oracle.int8_roundtrip(k[:, h])
+        for qb in range(2):
+            keys = np.array([r for b in list(prot) + list(tiles[h, qb])
+                             for r in range(16 * b, 16 * b + 16) if r < n])
+            ref_o, ref_l = _brute_dense_rows(qd, kd, v64[:, h], seg, t, wl.tara, wl.scale,
+                                            range(16 * qb, 16 * qb + 16), keys)
+            go, gl = got[(h, qb)]
+            assert np.max(np.abs(go - ref_o)) < 1e-12 and np.max(np.abs(gl - ref_l)) < 1e-12
+            assert np.max(np.abs(gl - plain[(h, qb)][1])) > 1e-6
