@@ -432,6 +432,22 @@ def main():
         next_rows["audio_sink_queries"] = row
         print("# routing variants done", file=sys.stderr, flush=True)
 
+        # int8 QK product on the attended tiles (per-token quantization of q and k inside
+        # the call), block 64, same router lists
+        ws_i8 = torch.empty(api.int8qk_workspace_bytes(N, H, D), dtype=torch.uint8,
+                            device="cuda")
+        row = time_pair(
+            lambda: api.attn_block_router(qd, kd, segd, wl.protected_prefix_len, k_sel, n_prot,
+                                          tiles=tiles, prot=prot, ws=ws_router),
+            lambda: api.attn_block_sparse_int8qk(qd, kd, vd, segd, td, tiles, prot, None, None,
+                                                 0, *tara, scale=scale, o=o_sparse,
+                                                 lse=l_sparse, ws=ws_i8))
+        row.update({"sparsity": args.sparsity, "block_size": 64,
+                    "note": "sparse_ms includes the int8 quantization of q and k"})
+        next_rows["int8_qk"] = row
+        del ws_i8
+        print("# int8 QK done", file=sys.stderr, flush=True)
+
     roofline = None
     if d:
         traffic = None

@@ -27,6 +27,7 @@ EXPORTS = (
     "attn_block_sparse_workspace", "attn_block_sparse",
     "attn_block_router_tail_workspace", "attn_block_router_tail", "attn_block_sparse_tail",
     "attn_block_sparse_sinks",
+    "attn_quantize_int8", "attn_block_sparse_int8qk_workspace", "attn_block_sparse_int8qk",
     "partition_lse_merge",
     "attn_dense_tara_via_workspace", "attn_dense_tara_via",
 )
@@ -54,6 +55,11 @@ _SIGS = {
     "attn_block_sparse_sinks": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f,
                                      _f, _i, _vp, _i, _vp, _i, _vp, _vp, ctypes.c_uint, _vp,
                                      _i, _vp, _vp, _sz, _vp]),
+    "attn_quantize_int8": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "attn_block_sparse_int8qk_workspace": (_sz, [_i, _i, _i]),
+    "attn_block_sparse_int8qk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _f, _f, _f, _f,
+                                      _f, _i, _vp, _i, _vp, _i, _vp, _vp, ctypes.c_uint, _vp,
+                                      _i, _vp, _vp, _sz, _vp]),
     "partition_lse_merge": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _vp]),
     "attn_dense_tara_via_workspace": (_sz, [_vp, _vp, _i, _i, _i, _i]),
     "attn_dense_tara_via": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -328,6 +334,57 @@ def attn_block_sparse_sinks(q, k, v, seg, t, tiles, prot, sink_segments, tail_ls
                                        int(sink_segments), _ptr(o), _dtype_code(o), _ptr(lse),
                                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check("attn_block_sparse_sinks", st)
+    return o, lse
+
+
+def quantize_int8(x, x8=None, scales=None, stream=None):
+    """Per-(row, head) int8 quantization: returns (x8 int8 [n, H, D], scales f32 [n, H])."""
+    import torch
+    n, H, D = x.shape
+    if x8 is None:
+        x8 = torch.empty((n, H, D), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, H), dtype=torch.float32, device=x.device)
+    _contig(x, x8, scales)
+    st = lib().attn_quantize_int8(_ptr(x), _dtype_code(x), n, H, D, _ptr(x8), _ptr(scales),
+                                  _stream(stream))
+    _check("attn_quantize_int8", st)
+    return x8, scales
+
+
+def int8qk_workspace_bytes(n, heads, head_dim):
+    return int(lib().attn_block_sparse_int8qk_workspace(n, heads, head_dim))
+
+
+def attn_block_sparse_int8qk(q, k, v, seg, t, tiles, prot, tail_lse=None, tail_v=None,
+                             sink_segments=0, strength=2.0, window=0.20, falloff=0.25, cap=6.0,
+                             scale=None, block_size=64, o=None, o_dtype=None, lse=None, ws=None,
+                             stream=None):
+    """Block-sparse attention with the per-token int8 QK product: returns (o, lse)."""
+    import torch
+    n, H, D = q.shape
+    dt = _dtype_code(q)
+    k_sel = int(tiles.shape[-1]) if tiles is not None else 0
+    n_prot = int(prot.numel()) if prot is not None else 0
+    if o is None:
+        o = _empty_like_out(q, o_dtype or q.dtype)
+    if lse is None:
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    if ws is None:
+        ws = _workspace(int8qk_workspace_bytes(n, H, D), q.device)
+    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    st = lib().attn_block_sparse_int8qk(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg),
+                                        _ptr(t), strength, window, falloff, cap, scale,
+                                        block_size, _ptr(tiles) if k_sel > 0 else None, k_sel,
+                                        _ptr(prot) if n_prot > 0 else None, n_prot,
+                                        _ptr(tail_lse) if tail_lse is not None else None,
+                                        _ptr(tail_v) if tail_v is not None else None,
+                                        int(sink_segments), _ptr(o), _dtype_code(o), _ptr(lse),
+                                        _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(stream))
+    _check("attn_block_sparse_int8qk", st)
     return o, lse
 
 

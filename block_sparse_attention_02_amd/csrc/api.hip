@@ -45,6 +45,13 @@ size_t attn_ws_bytes(int nk, int heads, int head_dim) {
   return align256(vt_bytes(nk, heads, head_dim)) + align256((size_t)pad_keys(nk) / kTile * sizeof(TileInfo));
 }
 
+// int8 QK workspace after the attention workspace: q8, k8 [n][heads][head_dim] int8 and
+// their scales [n][heads] float32, each 256-byte aligned.
+size_t int8_ws_bytes(int n, int heads, int head_dim) {
+  const size_t e = (size_t)n * heads * head_dim, p = (size_t)n * heads;
+  return 2 * align256(e) + 2 * align256(p * sizeof(float));
+}
+
 AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, int heads,
                    const uint8_t* q_seg, const float* q_t, const uint8_t* k_seg,
                    const float* k_t, float strength, float window, float falloff, float cap,
@@ -60,6 +67,7 @@ AttnArgs make_args(const void* q, const void* k, const void* v, int nq, int nk, 
   a.prot = nullptr; a.n_prot = 0; a.tiles = nullptr; a.k_sel = 0; a.nqb = 0;
   a.bs = kTile; a.sink_mask = 0u;
   a.tail_lse = nullptr; a.tail_v = nullptr;
+  a.q8 = nullptr; a.qsc = nullptr; a.k8 = nullptr; a.ksc = nullptr;
   return a;
 }
 
@@ -300,8 +308,8 @@ int sparse(const void* q, const void* k, const void* v, int dtype, int n, int he
            int head_dim, const uint8_t* seg, const float* t, float strength, float window,
            float falloff, float cap, float scale, int block_size, const int32_t* tiles,
            int k_sel, const int32_t* prot, int n_prot, const float* tail_lse,
-           const float* tail_v, uint32_t sink_mask, void* o, int o_dtype, float* lse, void* ws,
-           size_t ws_bytes, void* stream) {
+           const float* tail_v, uint32_t sink_mask, bool int8qk, void* o, int o_dtype,
+           float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !seg || !t || !o || !lse) return H3_EINVAL;
   if (n <= 0 || heads <= 0) return H3_EINVAL;
   if (k_sel < 0 || n_prot < 0 || k_sel + n_prot == 0) return H3_EINVAL;
@@ -312,10 +320,25 @@ int sparse(const void* q, const void* k, const void* v, int dtype, int n, int he
       heads > 65535)
     return H3_EUNSUPPORTED;
   if (!blocks_ok(n, block_size)) return H3_EUNSUPPORTED;
-  const size_t need = attn_dense_tara_workspace(n, heads, head_dim, dtype);
+  if (int8qk && (dtype != H3_DTYPE_BF16 || block_size == 32)) return H3_EUNSUPPORTED;
+  const size_t base = attn_dense_tara_workspace(n, heads, head_dim, dtype);
+  const size_t need = base + (int8qk ? int8_ws_bytes(n, heads, head_dim) : 0);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
   AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
                          scale, o, o_dtype, lse);
+  if (int8qk) {
+    const size_t e = (size_t)n * heads * head_dim, p = (size_t)n * heads;
+    char* w = (char*)ws + base;
+    int8_t* q8 = (int8_t*)w;
+    int8_t* k8 = (int8_t*)(w + align256(e));
+    float* qsc = (float*)(w + 2 * align256(e));
+    float* ksc = (float*)(w + 2 * align256(e) + align256(p * sizeof(float)));
+    hipError_t e1 = launch_quant_int8(q, true, (int64_t)p, head_dim, q8, qsc, (hipStream_t)stream);
+    if (e1 == hipSuccess)
+      e1 = launch_quant_int8(k, true, (int64_t)p, head_dim, k8, ksc, (hipStream_t)stream);
+    if (e1 != hipSuccess) return H3_ELAUNCH;
+    a.q8 = q8; a.qsc = qsc; a.k8 = k8; a.ksc = ksc;
+  }
   a.prot = prot;
   a.n_prot = n_prot;
   a.tiles = tiles;
@@ -361,8 +384,8 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype, in
                       const int32_t* tiles, int k_sel, const int32_t* prot, int n_prot, void* o,
                       int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
-                scale, block_size, tiles, k_sel, prot, n_prot, nullptr, nullptr, 0u, o, o_dtype,
-                lse, ws, ws_bytes, stream);
+                scale, block_size, tiles, k_sel, prot, n_prot, nullptr, nullptr, 0u, false, o,
+                o_dtype, lse, ws, ws_bytes, stream);
 }
 
 int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtype, int n,
@@ -373,8 +396,8 @@ int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtyp
                            int o_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!tail_lse || !tail_v) return H3_EINVAL;
   return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
-                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v, 0u, o, o_dtype,
-                lse, ws, ws_bytes, stream);
+                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v, 0u, false, o,
+                o_dtype, lse, ws, ws_bytes, stream);
 }
 
 int attn_block_sparse_sinks(const void* q, const void* k, const void* v, int dtype, int n,
@@ -387,7 +410,34 @@ int attn_block_sparse_sinks(const void* q, const void* k, const void* v, int dty
   if ((tail_lse == nullptr) != (tail_v == nullptr)) return H3_EINVAL;
   return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
                 scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v,
-                (uint32_t)sink_segments, o, o_dtype, lse, ws, ws_bytes, stream);
+                (uint32_t)sink_segments, false, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+size_t attn_block_sparse_int8qk_workspace(int n, int heads, int head_dim) {
+  if (n <= 0 || heads <= 0 || !dim_ok(head_dim)) return 0;
+  return attn_ws_bytes(n, heads, head_dim) + int8_ws_bytes(n, heads, head_dim);
+}
+
+int attn_block_sparse_int8qk(const void* q, const void* k, const void* v, int dtype, int n,
+                             int heads, int head_dim, const uint8_t* seg, const float* t,
+                             float strength, float window, float falloff, float cap,
+                             float scale, int block_size, const int32_t* tiles, int k_sel,
+                             const int32_t* prot, int n_prot, const float* tail_lse,
+                             const float* tail_v, unsigned sink_segments, void* o, int o_dtype,
+                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if ((tail_lse == nullptr) != (tail_v == nullptr)) return H3_EINVAL;
+  return sparse(q, k, v, dtype, n, heads, head_dim, seg, t, strength, window, falloff, cap,
+                scale, block_size, tiles, k_sel, prot, n_prot, tail_lse, tail_v,
+                (uint32_t)sink_segments, true, o, o_dtype, lse, ws, ws_bytes, stream);
+}
+
+int attn_quantize_int8(const void* x, int dtype, int rows, int heads, int head_dim, int8_t* x8,
+                       float* scales, void* stream) {
+  if (!x || !x8 || !scales || rows <= 0 || heads <= 0) return H3_EINVAL;
+  if (!dtype_ok(dtype) || !dim_ok(head_dim)) return H3_EUNSUPPORTED;
+  hipError_t e = launch_quant_int8(x, dtype == H3_DTYPE_BF16, (int64_t)rows * heads, head_dim,
+                                   x8, scales, (hipStream_t)stream);
+  return e == hipSuccess ? H3_OK : H3_ELAUNCH;
 }
 
 int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

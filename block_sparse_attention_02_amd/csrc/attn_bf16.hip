@@ -43,6 +43,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -169,6 +171,12 @@ struct Lds {
   static constexpr int KINS = KBYTES / 1024;  // 1 KB wave loads per K tile
   static constexpr int VINS = VBYTES / 1024;
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole wave loads");
+  // int8 K tiles (int8 QK product): rows of D bytes padded by 16
+  static constexpr int KRS8 = D + 16;
+  static constexpr int KSL8 = D / 16 + 1;
+  static constexpr int KBYTES8 = 64 * KRS8;
+  static constexpr int KINS8 = KBYTES8 / 1024;
+  static_assert(KBYTES8 % 1024 == 0 && KBYTES8 <= KBYTES, "int8 K tile");
 };
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;  // buffer offset that reads zero
 
@@ -204,7 +212,11 @@ __device__ __forceinline__ float pair_sum_swap(float x) {
 
 // FINE: block-sparse with 32-row routing blocks (per-wave lists, half tiles); a
 // separate instance so the 64/128-row kernel carries none of that code.
-template <int D, bool SPARSE, bool PEN, bool FINE = false>
+// Q8: block-sparse with the int8 QK product ("H3 SLA Attention", inputs table,
+// use_int8_qk): q and k come quantized per (row, head) (x8, scale); S = K8 Q8^T with
+// v_mfma_i32_32x32x32_i8, then each score is the int32 sum times the key's scale, and
+// the query's scale joins the exp factor. PV is unchanged (bf16 P, bf16 V).
+template <int D, bool SPARSE, bool PEN, bool FINE = false, bool Q8 = false>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NW = 8;               // waves per workgroup (two per SIMD)
   constexpr int BM = 32 * NW;         // query rows per workgroup
@@ -227,6 +239,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t vs2[L::VBYTES / 2];
   __shared__ uint8_t kseg0[64], kseg1[64], kseg2[64];
   __shared__ float kt0[64], kt1[64], kt2[64];
+  // int8 QK: per-key scales of the staged tiles
+  __shared__ __attribute__((aligned(16))) float ksc0[Q8 ? 64 : 4], ksc1[Q8 ? 64 : 4],
+      ksc2[Q8 ? 64 : 4];
   __shared__ int simd_waves[4];
   __shared__ int sink_waves;  // sparse: bit w = wave w's rows hold a sink-segment row
   // sparse: bitmap 0 = protected blocks, bitmap 1 + j = routed blocks of map j (see below)
@@ -244,18 +259,27 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* __restrict__ kp = (const uint16_t*)a.k;
   const uint16_t* __restrict__ vtp = a.vt;
   const TileInfo* __restrict__ tinfo = a.tinfo;
-  const float c_log2 = a.scale * kLog2e;
+  float c_log2 = a.scale * kLog2e;
 
   const int qrow = qblk * BM + wave * 32 + l32;
   const bool qvalid = qrow < a.nq;
-  bf16x8 qreg[DK];
+  bf16x8 qreg[Q8 ? 1 : DK];
+  i32x4 q8reg[Q8 ? D / 32 : 1];
+  if constexpr (Q8) {
 #pragma unroll
-  for (int s = 0; s < DK; ++s) {
-    if (qvalid) {
-      qreg[s] = *(const bf16x8*)(qp + ((int64_t)qrow * H + h) * D + 16 * s + 8 * hh);
-    } else {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qreg[s] = __builtin_bit_cast(bf16x8, z);
+    for (int s = 0; s < D / 32; ++s)
+      q8reg[s] = qvalid ? *(const i32x4*)(a.q8 + ((int64_t)qrow * H + h) * D + 32 * s + 16 * hh)
+                        : i32x4{0, 0, 0, 0};
+    c_log2 *= qvalid ? a.qsc[(int64_t)qrow * H + h] : 0.f;  // the query's scale
+  } else {
+#pragma unroll
+    for (int s = 0; s < DK; ++s) {
+      if (qvalid) {
+        qreg[s] = *(const bf16x8*)(qp + ((int64_t)qrow * H + h) * D + 16 * s + 8 * hh);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qreg[s] = __builtin_bit_cast(bf16x8, z);
+      }
     }
   }
   const float qt = qvalid ? a.q_t[qrow] : 0.f;
@@ -340,9 +364,15 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < KDMA; ++j) {
     const int slot = (wave + NW * j) * 64 + lane;
-    const int r = slot / L::KSL, c = slot % L::KSL;
-    koff[j] = c == L::KSL - 1 ? kOutOfRange
-                              : (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)(c * 16);
+    if constexpr (Q8) {
+      const int r = slot / L::KSL8, c = slot % L::KSL8;
+      koff[j] = c == L::KSL8 - 1 ? kOutOfRange
+                                 : (uint32_t)r * (uint32_t)(H * D) + (uint32_t)(c * 16);
+    } else {
+      const int r = slot / L::KSL, c = slot % L::KSL;
+      koff[j] = c == L::KSL - 1 ? kOutOfRange
+                                : (uint32_t)r * (uint32_t)(H * D * 2) + (uint32_t)(c * 16);
+    }
   }
 #pragma unroll
   for (int j = 0; j < VDMA; ++j) {
@@ -354,12 +384,21 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   auto dma_k = [&](int kb, uint16_t* kdst) __attribute__((always_inline)) {
     const int k0 = kb * 64;
     const int rows = min(64, a.nk - k0);
-    const void* kbase = kp + ((int64_t)k0 * H + h) * D;
-    const int kbytes = (rows - 1) * H * D * 2 + D * 2;
+    if constexpr (Q8) {
+      const void* kbase = a.k8 + ((int64_t)k0 * H + h) * D;
+      const int kbytes = (rows - 1) * H * D + D;
 #pragma unroll
-    for (int j = 0; j < KDMA; ++j)
-      if (wave + NW * j < L::KINS)
-        buffer_to_lds16(kbase, kbytes, (char*)kdst + (wave + NW * j) * 1024, koff[j]);
+      for (int j = 0; j < KDMA; ++j)
+        if (wave + NW * j < L::KINS8)
+          buffer_to_lds16(kbase, kbytes, (char*)kdst + (wave + NW * j) * 1024, koff[j]);
+    } else {
+      const void* kbase = kp + ((int64_t)k0 * H + h) * D;
+      const int kbytes = (rows - 1) * H * D * 2 + D * 2;
+#pragma unroll
+      for (int j = 0; j < KDMA; ++j)
+        if (wave + NW * j < L::KINS)
+          buffer_to_lds16(kbase, kbytes, (char*)kdst + (wave + NW * j) * 1024, koff[j]);
+    }
   };
   auto dma_v = [&](int kb, uint16_t* vdst) __attribute__((always_inline)) {
     const void* vbase = vtp + (int64_t)h * D * a.nkp + kb * 64;
@@ -385,6 +424,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       sg[tid] = (uint8_t)sreg;
       tt[tid] = treg;
     }
+  };
+  // int8 QK: the key scales of a tile (every tile), staged like the key rows above
+  float kscr = 0.f;
+  auto scale_load = [&](int kb) __attribute__((always_inline)) {
+    if (tid < 64) {
+      const int key = kb * 64 + tid;
+      kscr = key < a.nk ? a.ksc[(int64_t)key * H + h] : 0.f;
+    }
+  };
+  auto scale_store = [&](float* sc) __attribute__((always_inline)) {
+    if (tid < 64) sc[tid] = kscr;
   };
 
   // ---- tile classes: a tile is "fast" for this workgroup when all 64 keys are
@@ -498,6 +548,19 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
       for (int c = 0; c < NT; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
+      if constexpr (Q8) {  // int32 sums in the score registers until the softmax slot
+        const char* ksb = (const char*)kst + l32 * L::KRS8 + hh * 16;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const i32x4 ka = *(const i32x4*)(ksb + c * 32 * L::KRS8 + s * 32);
+            sacc[c] = __builtin_bit_cast(
+                f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            ka, q8reg[s], __builtin_bit_cast(i32x16, sacc[c]), 0, 0, 0));
+          }
+        }
+      } else {
       const char* ksb = (const char*)kst + l32 * L::KRS + hh * 16;
 #pragma unroll
       for (int s = 0; s < DK; ++s) {
@@ -506,6 +569,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
           const bf16x8 ka = *(const bf16x8*)(ksb + c * 32 * L::KRS + s * 32);
           sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
         }
+      }
       }
     }
   };
@@ -565,8 +629,22 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
   // -inf) does the tile take the maximum, rescale and exponentiate again. Probabilities
   // thus stay at most 2^8 while most tiles skip the maximum altogether.
   auto softmax_slot = [&](auto general_tag, const uint8_t* ksg, const float* ktt,
-                          const Tile& tl) __attribute__((always_inline)) {
+                          const float* kst8, const Tile& tl) __attribute__((always_inline)) {
     constexpr bool GENERAL = decltype(general_tag)::value;
+    if constexpr (Q8) {  // int32 sums -> float scores times each key's scale
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        // whole-vector casts: the int32 sums live in the score registers
+        f32x16 sf = __builtin_convertvector(__builtin_bit_cast(i32x16, sacc[c]), f32x16);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 sk = *(const f32x4*)(kst8 + 32 * c + 8 * g + 4 * hh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sf[4 * g + i] *= sk[i];
+        }
+        sacc[c] = sf;
+      }
+    }
     // block size 32: this wave may attend only one half of the tile (keys 0-31 or 32-63);
     // the other half gets a -inf bias
     const int h2 = fine ? (tl.qmask >> my_shift) & 3 : 3;
@@ -654,42 +732,48 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
     dma_k(tq.kb, ks0);
     dma_v(tq.kb, vs0);
     if (GENERAL) small_load(tq.kb);
+    if (Q8) scale_load(tq.kb);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (GENERAL) small_store(kseg0, kt0);
+    if (Q8) scale_store(ksc0);
     if (tn.kb < ntiles) {
       dma_k(tn.kb, ks1);
       if (GENERAL) small_load(tn.kb);
+      if (Q8) scale_load(tn.kb);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       if (GENERAL) small_store(kseg1, kt1);
+      if (Q8) scale_store(ksc1);
     }
     slot_barrier<kWaitAll0>();
     if (grp_b) slot_barrier<kWaitAll0>();
     // One (matrix, softmax) slot pair; the stage arguments rotate with j % 3.
     auto step = [&](uint16_t* kcur, uint16_t* vprev, uint16_t* knn, uint16_t* vnext,
-                    uint8_t* sgcur, float* ttcur, uint8_t* sgnext, float* ttnext)
-        __attribute__((always_inline)) {
+                    uint8_t* sgcur, float* ttcur, uint8_t* sgnext, float* ttnext,
+                    float* sccur, float* scnext) __attribute__((always_inline)) {
       mfma_slot(kcur, vprev, attends(tp), attends(tq));
       // the key rows of tile j+1 were fetched during the previous softmax slot
       if (GENERAL && tn.kb < ntiles) small_store(sgnext, ttnext);
+      if (Q8 && tn.kb < ntiles) scale_store(scnext);
       slot_barrier<kWaitAll0>();
       const Tile tnn = cursor_next(cu, !GENERAL);
       if (tnn.kb < ntiles) {
         dma_k(tnn.kb, knn);
         if (GENERAL) small_load(tnn.kb);
+        if (Q8) scale_load(tnn.kb);
       }
       if (tn.kb < ntiles) dma_v(tn.kb, vnext);
-      if (attends(tq)) softmax_slot(general_tag, sgcur, ttcur, tq);
+      if (attends(tq)) softmax_slot(general_tag, sgcur, ttcur, sccur, tq);
       slot_barrier<kWaitLgkm0>();
       tp = tq;
       tq = tn;
       tn = tnn;
     };
     while (true) {
-      step(ks0, vs2, ks2, vs1, kseg0, kt0, kseg1, kt1);
+      step(ks0, vs2, ks2, vs1, kseg0, kt0, kseg1, kt1, ksc0, ksc1);
       if (tp.kb >= ntiles) break;
-      step(ks1, vs0, ks0, vs2, kseg1, kt1, kseg2, kt2);
+      step(ks1, vs0, ks0, vs2, kseg1, kt1, kseg2, kt2, ksc1, ksc2);
       if (tp.kb >= ntiles) break;
-      step(ks2, vs1, ks1, vs0, kseg2, kt2, kseg0, kt0);
+      step(ks2, vs1, ks1, vs0, kseg2, kt2, kseg0, kt0, ksc2, ksc0);
       if (tp.kb >= ntiles) break;
     }
     if (!grp_b) slot_barrier<kWaitAll0>();
@@ -751,6 +835,10 @@ template <int D, bool SPARSE, bool PEN>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.nq + 255) / 256, a.H);
   if constexpr (SPARSE) {
+    if (a.q8) {  // int8 QK (block sizes 64 and 128)
+      attn_bf16_kernel<D, true, PEN, false, true><<<grid, 512, 0, s>>>(a);
+      return hipGetLastError();
+    }
     if (a.bs == 32) {
       attn_bf16_kernel<D, true, PEN, true><<<grid, 512, 0, s>>>(a);
       return hipGetLastError();

@@ -58,6 +58,12 @@ struct AttnArgs {
   // optional tail key per query block (block-sparse with tail term), else null
   const float* tail_lse;    // [H][nqb] natural log
   const float* tail_v;      // [H][nqb][D]
+  // int8 QK product (block-sparse, bf16 path), else null: per-(row, head) int8 q and k
+  // with their float32 scales
+  const int8_t* q8;         // [nq][H][D]
+  const float* qsc;         // [nq][H]
+  const int8_t* k8;         // [nk][H][D]
+  const float* ksc;         // [nk][H]
 };
 
 // Rounds a key count up to whole 64-key tiles.
@@ -69,6 +75,9 @@ hipError_t launch_vt_transpose(const uint16_t* v, uint16_t* vt, int nk, int H, i
 hipError_t launch_tile_info(const uint8_t* k_seg, const float* k_t, int nk, TileInfo* info,
                             hipStream_t s);
 hipError_t launch_attn_bf16(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
+// Per-(row, head) int8 quantization (see quant.hip); pairs = rows * heads.
+hipError_t launch_quant_int8(const void* x, bool bf16, int64_t pairs, int D, int8_t* x8,
+                             float* sc, hipStream_t s);
 // float32 path.
 hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, hipStream_t s);
 

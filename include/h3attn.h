@@ -241,6 +241,47 @@ int attn_block_sparse_sinks(const void* q, const void* k, const void* v, int dty
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Per-token int8 quantization.
+ * From "H3 SLA Attention", inputs table (use_int8_qk): Q and K are quantized to
+ * int8 per token with a dynamic scale. Reading (the page gives no formula): for
+ * each (row, head) vector x of head_dim values, in float32 with correct
+ * rounding, s = max|x| / 127 and x8 = clamp(rint(x / s), -127, 127), rounding
+ * half to even; a zero vector gives s = 0 and zeros.
+ * x:      device [rows][heads][head_dim], dtype H3_DTYPE_BF16 or H3_DTYPE_F32.
+ * x8:     device int8 [rows][heads][head_dim]; scales: device float32 [rows][heads].
+ * Errors: H3_EINVAL (null pointer, rows <= 0, heads <= 0); H3_EUNSUPPORTED
+ * (dtype, head_dim); H3_ELAUNCH.
+ */
+int attn_quantize_int8(const void* x, int dtype, int rows, int heads, int head_dim,
+                       int8_t* x8, float* scales, void* stream);
+
+/*
+ * Block-sparse attention with the int8 QK product.
+ * From "H3 SLA Attention", inputs table (use_int8_qk): Q and K are quantized to
+ * int8 per token (attn_quantize_int8) before the QK product on the attended
+ * blocks; the PV product stays as in attn_block_sparse. Scores are
+ * scale * s_q * s_k * sum_d q8 k8 - penalty, i.e. the score rule on the
+ * dequantized q and k. Otherwise as attn_block_sparse_sinks (optional tail
+ * terms, sink segments; pass 0 for none). bf16 inputs and block sizes 64 and
+ * 128 only.
+ * Workspace: attn_block_sparse_int8qk_workspace(n, heads, head_dim) bytes: the
+ * attn_block_sparse workspace followed by the int8 copies of q and k and their
+ * scales.
+ * Errors: as attn_block_sparse_sinks, plus H3_EUNSUPPORTED for float32 inputs or
+ * block_size 32.
+ */
+size_t attn_block_sparse_int8qk_workspace(int n, int heads, int head_dim);
+int attn_block_sparse_int8qk(const void* q, const void* k, const void* v, int dtype,
+                             int n, int heads, int head_dim,
+                             const uint8_t* seg, const float* t,
+                             float strength, float window, float falloff, float cap,
+                             float scale, int block_size, const int32_t* tiles, int k_sel,
+                             const int32_t* prot, int n_prot,
+                             const float* tail_lse, const float* tail_v,
+                             unsigned sink_segments, void* o, int o_dtype, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Stable LSE merge of one partition result into an accumulator, in place.
  * From "Flash Partitions for H3 native temporal alignment", section 4:
  *   adjusted_L = lse_i + log_w (+ log_w_rows[row][h] when non-NULL),

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     assert set(names) == set(api.EXPORTS)
     L = api.lib()
     for n in names:
@@ -262,3 +262,32 @@ def test_sink_entry_point_rejects_bad_arguments():
     bad = list(sp)
     bad[14] = 96
     assert L.attn_block_sparse_sinks(*bad, *tail, 1 << 2, P, 1, P, None, 0, None) == -2
+
+
+def test_int8_entry_points_reject_bad_arguments():
+    """int8 QK: quantization and sparse-attention argument checks before any HIP call; the
+    workspace adds int8 copies of q and k and one float32 scale per (row, head)."""
+    L = api.lib()
+    P = ctypes.c_void_p(16)
+    n, H, D = 1000, 2, 64
+    assert (L.attn_block_sparse_int8qk_workspace(n, H, D)
+            == L.attn_block_sparse_workspace(n, H, D, 1) + 2 * _a256(n * H * D)
+            + 2 * _a256(n * H * 4))
+    assert L.attn_block_sparse_int8qk_workspace(n, H, 96) == 0
+    assert L.attn_quantize_int8(None, 1, 10, 2, 64, P, P, None) == -1
+    assert L.attn_quantize_int8(P, 1, 0, 2, 64, P, P, None) == -1
+    assert L.attn_quantize_int8(P, 1, 10, 2, 64, None, P, None) == -1
+    assert L.attn_quantize_int8(P, 4, 10, 2, 64, P, P, None) == -2
+    assert L.attn_quantize_int8(P, 1, 10, 2, 80, P, P, None) == -2
+    sp = [P, P, P, 1, n, H, D, P, P, 2.0, 0.2, 0.25, 6.0, 0.125, 64, P, 4, P, 1]
+    rest = [P, 1, P, None, 0, None]
+    assert L.attn_block_sparse_int8qk(*sp, None, None, 0, *rest) == -4
+    assert L.attn_block_sparse_int8qk(*sp, P, P, 1 << 2, *rest) == -4
+    assert L.attn_block_sparse_int8qk(*sp, P, None, 0, *rest) == -1
+    assert L.attn_block_sparse_int8qk(*sp, None, None, 1 << 5, *rest) == -1
+    bad = list(sp)
+    bad[3] = 0          # float32 inputs
+    assert L.attn_block_sparse_int8qk(*bad, None, None, 0, *rest) == -2
+    bad = list(sp)
+    bad[14] = 32        # 32-row blocks
+    assert L.attn_block_sparse_int8qk(*bad, None, None, 0, *rest) == -2

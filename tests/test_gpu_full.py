@@ -224,3 +224,30 @@ def test_full_block_sizes_with_audio_sinks_sampled(full, bs):
     assert blocks[-1] == nb - 1
     compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
             f"full sparse bs={bs} audio sinks")
+
+
+def test_full_sparse_int8qk_sampled(full):
+    """Full scale, s = 0.90, block 64, TARA on routed guide tiles, int8 QK product:
+    sampled rows against the oracle's attention on the dequantized q and k."""
+    wl, seg, t, dev, host, host32 = full
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.90)
+    print("router + int8 QK sparse 116883 x 56, s=0.90", flush=True)
+    tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
+                                        plan["k_sel"], plan["n_prot"])
+    o, lse = api.attn_block_sparse_int8qk(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"],
+                                          tiles, prot, None, None, 0, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    tl = tiles.cpu().numpy()[HEADS]
+    blocks = _blocks()
+    ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64,
+                              prot.cpu().numpy(), tl, heads=range(len(HEADS)), qblocks=blocks,
+                              int8_qk=True)
+    og, lg, orf, lrf = [], [], [], []
+    for (j, qb), (ob, lb) in ref.items():
+        lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
+        og.append(o[lo:hi, HEADS[j]])
+        lg.append(lse[lo:hi, HEADS[j]])
+        orf.append(ob)
+        lrf.append(lb)
+    compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
+            "full sparse int8 QK s=0.9")
