@@ -40,11 +40,11 @@ def test_quantize_int8_bit_exact(dtype, d):
     assert list(got8[9, 1, :4]) == [64, 127, 64, 127]
 
 
-def _case(heads=3, seed=130, tail_rows=19):
+def _case(heads=3, seed=130, tail_rows=19, d=128):
     spans = [W.Span(W.SEG_TEXT, 100), W.Span(W.SEG_GUIDE, 8 * 130, 8),
              W.Span(W.SEG_AUDIO, 60), W.Span(W.SEG_OUTPUT, 8 * 130, 8),
              W.Span(W.SEG_TEXT, tail_rows)]
-    return W.custom(f"i8_{seed}", spans, heads=heads, head_dim=128, dtype="bf16",
+    return W.custom(f"i8_{seed}_{d}", spans, heads=heads, head_dim=d, dtype="bf16",
                     seed_index=seed, frame_weight=0.7, protected_prefix_len=100)
 
 
@@ -57,21 +57,23 @@ def _assemble(ref, n, heads, d, bs):
     return o_ref, l_ref
 
 
-@pytest.mark.parametrize("bs,sparsity,tail,sinks", [(64, 0.5, False, False),
-                                                    (64, 0.9, False, False),
-                                                    (64, 0.8, True, True),
-                                                    (128, 0.85, True, False),
-                                                    (128, 0.7, False, True)])
-def test_sparse_int8qk_small(bs, sparsity, tail, sinks):
+@pytest.mark.parametrize("bs,sparsity,tail,sinks,d", [(64, 0.5, False, False, 128),
+                                                      (64, 0.9, False, False, 128),
+                                                      (64, 0.8, True, True, 128),
+                                                      (128, 0.85, True, False, 128),
+                                                      (128, 0.7, False, True, 128),
+                                                      (64, 0.85, True, True, 64),
+                                                      (128, 0.6, False, False, 64)])
+def test_sparse_int8qk_small(bs, sparsity, tail, sinks, d):
     """Router + int8 QK sparse attention (TARA penalty on routed guide tiles, optional
     tail terms and audio sink blocks); every output row against the oracle's int8 path.
     The result also differs measurably from the bf16 QK path."""
-    wl = _case()
+    wl = _case(d=d)
     seg, t, seg_d, t_d = layout_device(wl)
     q, k, v = W.make_qkv(wl)
     qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
     plan = api.router_plan(seg, 100, sparsity, block_size=bs)
-    print(f"case int8 bs={bs} s={sparsity} tail={tail} sinks={sinks}", flush=True)
+    print(f"case int8 bs={bs} s={sparsity} tail={tail} sinks={sinks} d={d}", flush=True)
     if tail:
         tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, 100, plan["k_sel"],
                                                          plan["n_prot"], scale=wl.scale,
@@ -91,8 +93,9 @@ def test_sparse_int8qk_small(bs, sparsity, tail, sinks):
     ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
                               wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails,
                               sink_segments=(W.SEG_AUDIO,) if sinks else (), int8_qk=True)
-    o_ref, l_ref = _assemble(ref, wl.n, 3, 128, bs)
-    compare(o, lse, o_ref, l_ref, "bf16", f"int8 bs={bs} s={sparsity} tail={tail} sinks={sinks}")
+    o_ref, l_ref = _assemble(ref, wl.n, 3, d, bs)
+    compare(o, lse, o_ref, l_ref, "bf16",
+            f"int8 bs={bs} s={sparsity} tail={tail} sinks={sinks} d={d}")
     diff = float(np.max(np.abs(l16.cpu().numpy() - lse.cpu().numpy())))
     print(f"int8 vs bf16 QK lse difference {diff:.2e}", flush=True)
     assert diff > 1e-4

@@ -17,8 +17,8 @@ pytestmark = pytest.mark.gpu
 AUDIO_SINK = 1 << W.SEG_AUDIO
 
 
-def _pen_case(dtype, heads=3, seed=120, tail_rows=0):
-    d = 128 if dtype == "bf16" else 64
+def _pen_case(dtype, heads=3, seed=120, tail_rows=0, d=None):
+    d = d or (128 if dtype == "bf16" else 64)
     spans = [W.Span(W.SEG_TEXT, 100), W.Span(W.SEG_GUIDE, 8 * 130, 8),
              W.Span(W.SEG_AUDIO, 60), W.Span(W.SEG_OUTPUT, 8 * 130, 8)]
     if tail_rows:
@@ -121,12 +121,12 @@ def test_sparse_block_sizes_small(bs, dtype, sparsity, tail):
 
 
 @pytest.mark.parametrize("bs", [32, 128])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_sparse_block_sizes_hand_built_lists(bs, dtype):
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_sparse_block_sizes_hand_built_lists(bs, dtype, d):
     """Random lists per block with repeats, -1 and out-of-range entries, a protected list
     out of order: at block size 32 neighbouring 32-row blocks pick different halves of
     the same 64-key tiles."""
-    wl = _pen_case(dtype, heads=2, seed=121, tail_rows=45)
+    wl = _pen_case(dtype, heads=2, seed=121, tail_rows=45, d=d)
     seg, t, seg_d, t_d = layout_device(wl)
     q, k, v = W.make_qkv(wl)
     qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
@@ -138,7 +138,7 @@ def test_sparse_block_sizes_hand_built_lists(bs, dtype):
     tl[:, ::3, 2] = -1
     tl[:, ::5, 3] = nb + 4
     prot = np.array([3, 0, nb - 1], dtype=np.int32)
-    print(f"case hand lists bs={bs} {dtype} n={wl.n}", flush=True)
+    print(f"case hand lists bs={bs} {dtype} d={d} n={wl.n}", flush=True)
     o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, torch.from_numpy(tl).cuda(),
                                    torch.from_numpy(prot).cuda(), *wl.tara, scale=wl.scale,
                                    block_size=bs)
@@ -146,7 +146,7 @@ def test_sparse_block_sizes_hand_built_lists(bs, dtype):
     ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
                               wl.scale, bs, prot, tl)
     o_ref, l_ref = _assemble(ref, wl.n, 2, wl.head_dim, bs)
-    compare(o, lse, o_ref, l_ref, dtype, f"hand lists bs={bs} {dtype}")
+    compare(o, lse, o_ref, l_ref, dtype, f"hand lists bs={bs} {dtype} d={d}")
 
 
 @pytest.mark.parametrize("bs", [32, 64, 128])
