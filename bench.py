@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/call + dense-equiv TFLOP/s (%MFMA peak), 116,883 rows x 56 heads, 1 GPU"
-DENSE_KERNEL = "attn_bf16_kernel<128, false, true>"
+DENSE_KERNEL = "attn_bf16_kernel<128, false, true, false, false>"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_dense_tara_116883x56_pmc.json")
 
 
