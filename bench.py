@@ -38,11 +38,20 @@ DENSE_KERNEL = "attn_bf16_kernel<128, false, true, false, false>"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_dense_tara_116883x56_pmc.json")
 
 
-def kernel_source_hash():
+def code_hash(text):
+    """Hash of the code lines of a HIP source: // comments and blank lines do not count, so
+    a comment edit leaves the compiled kernel, and its counter summary, valid."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "block_sparse_attention_02_amd", "csrc", "attn_bf16.hip"), "rb") as f:
-        h.update(f.read())
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash():
+    with open(os.path.join(ROOT, "block_sparse_attention_02_amd", "csrc", "attn_bf16.hip")) as f:
+        return code_hash(f.read())
 
 
 def parse():

@@ -1,4 +1,4 @@
-// bf16 attention for gfx950: dense TARA and block-sparse over 64-key tiles.
+// bf16 attention for gfx950: dense TARA and block-sparse attention over 64-key tiles.
 //
 // Score rule ("Flash Partitions for H3 native temporal alignment", section 1):
 //   s_ij = scale * q_i.k_j - p_ij, p_ij = min(strength*(max(|t_i-t_j|-window,0)/falloff)^2, cap)
@@ -12,12 +12,15 @@
 // workgroup; wave w owns rows 32w..32w+31 and all 64 keys of each tile, so each K/V
 // tile load serves up to 256 queries.
 //   dense : every key tile, in order;
-//   sparse: the workgroup's rows are four 64-row query blocks. Their attended tiles
-//           (the protected tiles plus each block's routed tiles) are collected as bitmaps
-//           in LDS, and the workgroup walks the union in ascending tile order: every tile
-//           is loaded once for all four blocks and each wave computes only the tiles its
-//           own block attends. Routed lists of neighbouring blocks overlap heavily when
-//           the blocks share a video frame, so most loads serve the whole workgroup.
+//   sparse: the workgroup's rows are four 64-row query blocks (or halves of two 128-row
+//           blocks, or eight 32-row blocks, one per wave). Their attended tiles (the
+//           protected tiles plus each block's routed tiles, or every tile for a sink
+//           block) are collected as bitmaps in LDS, and the workgroup walks the union in
+//           ascending tile order: every tile is loaded once for all its blocks and each
+//           wave computes only the tiles (or, for 32-row blocks, the tile halves) its own
+//           block attends. Routed lists of neighbouring blocks overlap heavily when the
+//           blocks share a video frame, so most loads serve the whole workgroup.
+//           Optional: a pooled tail key merged in the epilogue, and an int8 QK product.
 // Matrix cores: S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so each
 // lane holds one query column; softmax row reductions stay in registers plus one
 // exchange between lane halves.
