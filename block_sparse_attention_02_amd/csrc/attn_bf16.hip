@@ -188,6 +188,22 @@ constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitAll0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
 
+// Scheduling order for a run of N MFMAs, each fed by one LDS operand read: AHEAD reads
+// are issued first and one more after every MFMA, so AHEAD reads stay in flight and the
+// MFMAs do not wait out each read's full LDS latency.
+template <int N, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  constexpr int A = N > AHEAD ? AHEAD : N;  // a short run: every read first
+  __builtin_amdgcn_sched_group_barrier(0x100, A, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+constexpr int kLdsAhead = 4;
+
 // Workgroup barrier without the memory-model fence of __syncthreads (that fence would
 // also wait for the direct-to-LDS loads meant to stay in flight across it). WAIT is
 // the s_waitcnt the caller needs before arriving; the empty asm statements keep the
@@ -543,6 +559,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
         }
       }
+      pipeline_lds_mfma<DT * NS, kLdsAhead>();
     }
     // keep the two products apart so their operand reads do not pile up in registers
     __builtin_amdgcn_sched_barrier(0);
@@ -563,6 +580,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
                             ka, q8reg[s], __builtin_bit_cast(i32x16, sacc[c]), 0, 0, 0));
           }
         }
+        pipeline_lds_mfma<(D / 32) * NT, kLdsAhead>();
       } else {
       const char* ksb = (const char*)kst + l32 * L::KRS + hh * 16;
 #pragma unroll
@@ -573,6 +591,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnArgs a) {
           sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], sacc[c], 0, 0, 0);
         }
       }
+      pipeline_lds_mfma<DK * NT, kLdsAhead>();
       }
     }
   };
