@@ -1,0 +1,123 @@
+"""GPU edge cases of the routed paths against the oracle: a sequence shorter than one
+block, a sequence with no protected block, attention over the protected tiles only,
+tail terms that vanish at sparsity 0, and int8 inputs with all-zero rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_02_amd import api, workloads as W
+from gpu_common import compare, f64, layout_device, to_device
+from test_gpu_small import _route_oracle, _tails_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _assemble(ref, n, heads, d, bs):
+    o_ref = np.zeros((n, heads, d))
+    l_ref = np.zeros((n, heads))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * bs:qb * bs + len(ob), h] = ob
+        l_ref[qb * bs:qb * bs + len(ob), h] = lb
+    return o_ref, l_ref
+
+
+def _run(wl, prefix, sparsity, bs, dtype, tail=False, n_prot_override=None):
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    plan = api.router_plan(seg, prefix, sparsity, block_size=bs)
+    print(f"case {wl.name} bs={bs} {dtype} plan={plan} tail={tail}", flush=True)
+    if tail:
+        tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, prefix, plan["k_sel"],
+                                                         plan["n_prot"], scale=wl.scale,
+                                                         block_size=bs)
+        o, lse = api.attn_block_sparse_tail(qd, kd, vd, seg_d, t_d, tiles, prot, tl, tv,
+                                            *wl.tara, scale=wl.scale, block_size=bs)
+    else:
+        tiles, prot = api.attn_block_router(qd, kd, seg_d, prefix, plan["k_sel"], plan["n_prot"],
+                                            block_size=bs)
+        if plan["k_sel"] == 0:
+            tiles = None
+        o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot if plan["n_prot"] else None,
+                                       *wl.tara, scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    heads = wl.heads
+    nb = plan["nb"]
+    tl_np = (tiles.cpu().numpy() if tiles is not None
+             else np.zeros((heads, nb, 0), dtype=np.int32))
+    if plan["k_sel"]:
+        assert np.array_equal(tl_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(heads), bs=bs))
+    tails = _tails_oracle(wl, q, k, v, seg, tl_np, range(heads), bs=bs) if tail else None
+    pr = prot.cpu().numpy() if plan["n_prot"] else np.zeros(0, dtype=np.int32)
+    ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
+                              wl.scale, bs, pr, tl_np, tails=tails)
+    o_ref, l_ref = _assemble(ref, wl.n, heads, wl.head_dim, bs)
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} bs={bs} {dtype} tail={tail}")
+    return tails
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sequence_shorter_than_one_block(bs, dtype):
+    """23 rows (a single ragged block at every size): guide and output video only."""
+    d = 128 if dtype == "bf16" else 64
+    wl = W.custom(f"tiny_{bs}_{dtype}", [W.Span(W.SEG_GUIDE, 12, 2), W.Span(W.SEG_OUTPUT, 11, 2)],
+                  heads=2, head_dim=d, dtype=dtype, seed_index=140, frame_weight=0.7)
+    _run(wl, 0, 0.5, bs, dtype)
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_no_protected_block(bs):
+    """Only video rows and no protected prefix: the routed tiles are the whole key set."""
+    wl = W.custom(f"video_only_{bs}", [W.Span(W.SEG_GUIDE, 6 * 150, 6),
+                                       W.Span(W.SEG_OUTPUT, 6 * 150 + 13, 6)],
+                  heads=2, head_dim=128, dtype="bf16", seed_index=141, frame_weight=0.7)
+    _run(wl, 0, 0.8, bs, "bf16")
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_protected_tiles_only(bs):
+    """No video tile (text and audio only): k = 0, every block attends the protected set,
+    which is every key, so the result is plain attention."""
+    wl = W.custom(f"prot_only_{bs}", [W.Span(W.SEG_TEXT, 300), W.Span(W.SEG_AUDIO, 211)],
+                  heads=2, head_dim=128, dtype="bf16", seed_index=142)
+    _run(wl, 300, 0.9, bs, "bf16")
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_tail_vanishes_at_sparsity_zero(bs):
+    """Sparsity 0 routes every video tile: every tail logit is -inf and the result is
+    dense TARA."""
+    wl = W.custom(f"tail0_{bs}", [W.Span(W.SEG_TEXT, 70), W.Span(W.SEG_GUIDE, 5 * 90, 5),
+                                  W.Span(W.SEG_AUDIO, 30), W.Span(W.SEG_OUTPUT, 5 * 90, 5)],
+                  heads=2, head_dim=128, dtype="bf16", seed_index=143, frame_weight=0.7,
+                  protected_prefix_len=70)
+    tails = _run(wl, 70, 0.0, bs, "bf16", tail=True)
+    for h in tails:
+        assert np.all(np.isneginf(tails[h][0]))
+
+
+def test_int8_zero_rows():
+    """Query and key rows that are all zero quantize to zero with scale 0; the int8 path
+    still matches the oracle (those scores are 0)."""
+    wl = W.custom("i8_zero", [W.Span(W.SEG_TEXT, 64), W.Span(W.SEG_GUIDE, 4 * 96, 4),
+                              W.Span(W.SEG_OUTPUT, 4 * 96, 4)],
+                  heads=2, head_dim=128, dtype="bf16", seed_index=144, frame_weight=0.7,
+                  protected_prefix_len=64)
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    q[10:20] = 0
+    k[100:164] = 0                       # one whole key tile of zeros
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    plan = api.router_plan(seg, 64, 0.5)
+    tiles, prot = api.attn_block_router(qd, kd, seg_d, 64, plan["k_sel"], plan["n_prot"])
+    print("case int8 zero rows", flush=True)
+    o, lse = api.attn_block_sparse_int8qk(qd, kd, vd, seg_d, t_d, tiles, prot, None, None, 0,
+                                          *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
+                              wl.scale, 64, prot.cpu().numpy(), tiles.cpu().numpy(),
+                              int8_qk=True)
+    o_ref, l_ref = _assemble(ref, wl.n, 2, 128, 64)
+    compare(o, lse, o_ref, l_ref, "bf16", "int8 zero rows")
