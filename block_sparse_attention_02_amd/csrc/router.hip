@@ -17,8 +17,9 @@
 //                with ties to the lower tile index, emitted in ascending tile order.
 // With the tail term ("H3 SLA Attention", inputs table, tail_correction) the pool pass
 // also takes the mean of V, and the top-k kernel folds the unrouted video tiles of each
-// query block into one pooled key: logit ln sum_u n_u exp(scale * S[qb,u]) and value the
-// same-weighted mean of their V means, from the same float32 pooled scores.
+// query block into one pooled key: logit ln sum_u n_u exp(scale * S[qb,u]) from the same
+// float32 pooled scores, and normalised weights whose product with the V means (fp16 on
+// the matrix cores, float32 sums) gives the key's value.
 #include "h3_internal.h"
 
 #pragma clang fp contract(off)
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   if (!TAIL) return;
 
   // ---- tail term of each query block from the unrouted video tiles: weights in place
-  // of the scores, logit to tail.lse, then the weighted V means to tail.v
+  // of the scores, logit to tail.lse, then the normalised weights to tail.wts
   __shared__ float tsum[QB];
   if (active) {
     float* my_w = sc + w * nv;
@@ -341,36 +342,71 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
   }
   __syncthreads();
-  // weighted V means: thread (g, d) takes every GROUPS-th video tile for all QB query
-  // blocks at once (one vbar read serves QB products), then the groups are added
-  constexpr int GROUPS = 256 / D;
-  __shared__ float part[GROUPS > 1 ? (GROUPS - 1) * QB * D : 1];
-  const int d = tid % D, g = tid / D;
-  float acc[QB];
-#pragma unroll
-  for (int j = 0; j < QB; ++j) acc[j] = 0.f;
-  const float* vh = tail.vbar + (int64_t)h * nb * D + d;
-#pragma unroll 4
-  for (int i = g; i < nv; i += GROUPS) {
-    const float vb = vh[(int64_t)video[i] * D];
-#pragma unroll
-    for (int j = 0; j < QB; ++j) acc[j] += sc[j * nv + i] * vb;
-  }
-  if (g > 0) {
-#pragma unroll
-    for (int j = 0; j < QB; ++j) part[((g - 1) * QB + j) * D + d] = acc[j];
-  }
-  __syncthreads();
-  if (g == 0) {
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      for (int gg = 1; gg < GROUPS; ++gg) acc[j] += part[((gg - 1) * QB + j) * D + d];
-      const int qj = qb0 + j;
-      if (qj < nb) {
-        const float sm = tsum[j];
-        tail.v[((int64_t)h * nb + qj) * D + d] = sm > 0.f ? acc[j] / sm : 0.f;
-      }
+  // normalised weights as fp16 rows [qb][nbp] (zero for routed tiles and past nv); the
+  // weighted V means are one matrix product per head (tail_v_kernel)
+  if (active && qb < nb) {
+    const float* my_w = sc + w * nv;
+    const float sm = tsum[w];
+    const float inv = sm > 0.f ? 1.f / sm : 0.f;
+    uint16_t* row = tail.wts + ((int64_t)h * nb + qb) * tail.nbp;
+    for (int i = lane; i < tail.nbp; i += 64) {
+      const float wt = i < nv ? my_w[i] * inv : 0.f;
+      row[i] = __builtin_bit_cast(uint16_t, (_Float16)wt);
     }
+  }
+}
+
+// fp16 V means of the video tiles, transposed: vbt[h][d][i] = vbar[h][video[i]][d] for
+// i < n_video, zero up to nbp.
+template <int D>
+__global__ __launch_bounds__(256) void tail_vbar_kernel(const float* __restrict__ vbar,
+                                                        const int32_t* __restrict__ video,
+                                                        const int32_t* __restrict__ counts,
+                                                        int nb, int nbp,
+                                                        uint16_t* __restrict__ vbt) {
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int nv = counts[1];
+  const bool live = i < nv;
+  const int kb = live ? video[i] : 0;
+  for (int d = threadIdx.x >> 6; d < D; d += 4) {
+    const float x = live ? vbar[((int64_t)h * nb + kb) * D + d] : 0.f;
+    if (i < nbp) vbt[((int64_t)h * D + d) * nbp + i] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// tail_v[h][qb][:] = sum_i wts[h][qb][i] * vbt[h][:][i]: a [nb x nv] x [nv x D] product per
+// head on the matrix cores (fp16 inputs, float32 sums). Workgroup = 32 query blocks of one
+// head; wave w takes the 32 output columns 32w..32w+31.
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void tail_v_kernel(const uint16_t* __restrict__ wts,
+                                                               const uint16_t* __restrict__ vbt,
+                                                               const int32_t* __restrict__ counts,
+                                                               int nb, int nbp,
+                                                               float* __restrict__ tail_v) {
+  const int h = blockIdx.y;
+  const int qb0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int kend = (counts[1] + 15) & ~15;  // video tiles, in steps of 16 (<= nbp)
+  const bool row_ok = qb0 + l32 < nb;
+  const uint16_t* arow = wts + ((int64_t)h * nb + (row_ok ? qb0 + l32 : 0)) * nbp + 8 * hh;
+  const uint16_t* brow = vbt + ((int64_t)h * D + 32 * w + l32) * nbp + 8 * hh;
+  f32x16 acc = {};
+  for (int k0 = 0; k0 < kend; k0 += 16) {
+    f16x8 a = *(const f16x8*)(arow + k0);
+    if (!row_ok) a = f16x8{};
+    const f16x8 b = *(const f16x8*)(brow + k0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+  }
+  // lane holds column 32w + l32 and rows 8(r/4) + 4hh + r%4
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qb = qb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+    if (qb < nb) tail_v[((int64_t)h * nb + qb) * D + 32 * w + l32] = acc[r];
   }
 }
 
@@ -380,8 +416,12 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t router_ws_bytes(int n, int H, int D, int bs, bool tail) {
   const size_t nb = (size_t)((n + bs - 1) / bs);
+  const size_t nbp = (nb + 31) / 32 * 32;
   const size_t means = align256(nb * H * D * sizeof(float));
-  return (tail ? 3 : 2) * means + align256(nb * sizeof(int32_t)) + 256;
+  size_t b = 2 * means + align256(nb * sizeof(int32_t)) + 256;
+  if (tail)
+    b += means + align256((size_t)H * nb * nbp * 2) + align256((size_t)H * D * nbp * 2);
+  return b;
 }
 
 RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
@@ -397,7 +437,17 @@ RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
   p += align256(nb * sizeof(int32_t));
   w.counts = (int32_t*)p;
   p += 256;
-  w.vbar = tail ? (float*)p : nullptr;
+  w.vbar = nullptr;
+  w.wts = nullptr;
+  w.vbt = nullptr;
+  w.nbp = (int)((nb + 31) / 32 * 32);
+  if (tail) {
+    w.vbar = (float*)p;
+    p += means;
+    w.wts = (uint16_t*)p;
+    p += align256((size_t)H * nb * w.nbp * 2);
+    w.vbt = (uint16_t*)p;
+  }
   return w;
 }
 
@@ -434,10 +484,15 @@ void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, in
   const int qb = wide ? 4 : 1;
   dim3 tgrid((nb + qb - 1) / qb, H);
   const size_t lds = (size_t)qb * nb * sizeof(float);
+  if (TAIL) tail_vbar_kernel<D><<<dim3(w.nbp / 64 + 1, H), 256, 0, s>>>(w.vbar, w.video, w.counts,
+                                                                    nb, w.nbp, w.vbt);
   if (wide)
     launch_topk<D, 4, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
   else
     launch_topk<D, 1, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
+  if (TAIL)
+    tail_v_kernel<D><<<dim3((nb + 31) / 32, H), 64 * (D / 32), 0, s>>>(w.wts, w.vbt, w.counts, nb,
+                                                                      w.nbp, ta.v);
 }
 
 hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
@@ -450,7 +505,7 @@ hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool tail = tail_lse != nullptr;
-  const TailArgs ta{scale, n, bs, w.vbar, tail_lse, tail_v};
+  const TailArgs ta{scale, n, bs, w.vbar, tail_lse, tail_v, w.wts, w.nbp};
   if (D == 128) {
     if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
     else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
