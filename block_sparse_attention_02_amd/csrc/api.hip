@@ -26,6 +26,8 @@ int check_tara(float strength, float window, float falloff, float cap, float sca
 }
 
 bool dtype_ok(int dt) { return dt == H3_DTYPE_F32 || dt == H3_DTYPE_BF16; }
+// bf16 key sets: the transposed v copy is read through 32-bit buffer offsets
+constexpr int kMaxBf16Keys = 1 << 23;
 bool dim_ok(int d) { return d == 64 || d == 128; }
 bool bs_ok(int bs) { return bs == 32 || bs == 64 || bs == 128; }
 // Sequences the router and the block-sparse kernels take: at most kMaxBlocks blocks of
@@ -223,6 +225,7 @@ int attn_dense_tara(const void* q, const void* k, const void* v, int dtype, int 
   if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
   if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || heads > 65535)
     return H3_EUNSUPPORTED;
+  if (dtype == H3_DTYPE_BF16 && nk > kMaxBf16Keys) return H3_EUNSUPPORTED;
   const size_t need = attn_dense_tara_workspace(nk, heads, head_dim, dtype);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
   AttnArgs a = make_args(q, k, v, nq, nk, heads, q_seg, q_t, k_seg, k_t, strength, window,
@@ -469,6 +472,7 @@ int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, 
   if (int st = check_tara(strength, window, falloff, cap, scale)) return st;
   if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || heads > 65535)
     return H3_EUNSUPPORTED;
+  if (dtype == H3_DTYPE_BF16 && n > kMaxBf16Keys) return H3_EUNSUPPORTED;
   const ViaPlan p = make_plan(seg_host, t_host, n, heads, head_dim, dtype);
   if (!ws || ws_bytes < p.total) return H3_EWORKSPACE;
 

@@ -24,14 +24,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ o_ac
                                                         const float* __restrict__ log_w_rows,
                                                         int64_t pairs) {
   constexpr int LPP = D / 4;
-  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x; gt < pairs * LPP;
+       gt += (int64_t)gridDim.x * 256) {
   const int64_t pair = gt / LPP;
   const int part = (int)(gt % LPP);
-  if (pair >= pairs) return;
   const float a = lse_acc[pair];
   float b = lse_i[pair] + log_w;
   if (log_w_rows) b += log_w_rows[pair];
-  if (!(b > -INFINITY)) return;  // zero-weight part (or NaN normaliser): no-op
+  if (!(b > -INFINITY)) continue;  // zero-weight part (or NaN normaliser): no-op
   const float m = fmaxf(a, b);
   const float L = m + log1pf(expf(-fabsf(a - b)));
   const float wa = expf(a - L);
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ o_ac
   x = (a > -INFINITY) ? x * wa + y * wb : y * wb;
   *po = x;
   if (part == 0) lse_acc[pair] = L;
+  }
 }
 
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ o_acc,
@@ -84,12 +85,12 @@ inline int grid_for(int64_t work) {
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,
                             float log_w, const float* log_w_rows, int64_t pairs, int D,
                             hipStream_t s) {
-  const int64_t threads = pairs * (D / 4);
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (pairs * (D / 4) + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
   if (D == 128)
-    lse_merge_kernel<128><<<(unsigned)blocks, 256, 0, s>>>(o_acc, lse_acc, o_i, lse_i, log_w, log_w_rows, pairs);
+    lse_merge_kernel<128><<<grid, 256, 0, s>>>(o_acc, lse_acc, o_i, lse_i, log_w, log_w_rows, pairs);
   else
-    lse_merge_kernel<64><<<(unsigned)blocks, 256, 0, s>>>(o_acc, lse_acc, o_i, lse_i, log_w, log_w_rows, pairs);
+    lse_merge_kernel<64><<<grid, 256, 0, s>>>(o_acc, lse_acc, o_i, lse_i, log_w, log_w_rows, pairs);
   return hipGetLastError();
 }
 

@@ -20,7 +20,11 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const void* __restrict_
                                                          int8_t* __restrict__ x8,
                                                          float* __restrict__ sc) {
   constexpr int LPP = D / 8;
-  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // grid-stride over whole 256-thread rounds, so every lane of a (row, head) group runs
+  // the same iterations and takes part in the shuffles
+  const int64_t total = (pairs * LPP + 255) / 256 * 256;
+  for (int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x; gl < total;
+       gl += (int64_t)gridDim.x * 256) {
   const int64_t pair = gl / LPP;
   const int part = (int)(gl % LPP);
   const bool valid = pair < pairs;
@@ -59,14 +63,15 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const void* __restrict_
     *(u32x2*)(x8 + pair * D + part * 8) = u32x2{w[0], w[1]};
     if (part == 0) sc[pair] = s;
   }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quant_int8(const void* x, bool bf16, int64_t pairs, int D, int8_t* x8,
                              float* sc, hipStream_t s) {
-  const int64_t threads = pairs * (D / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t blocks = (pairs * (D / 8) + 255) / 256;
+  const dim3 grid((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20)));
   if (D == 128) {
     if (bf16) quant_int8_kernel<128, true><<<grid, 256, 0, s>>>(x, pairs, x8, sc);
     else quant_int8_kernel<128, false><<<grid, 256, 0, s>>>(x, pairs, x8, sc);

@@ -77,7 +77,9 @@ const char* h3attn_status_string(int status);
  * (0 for fp32); it holds a transposed copy of v used by the matrix cores.
  * Errors: H3_EINVAL for null pointers, nq/nk/heads <= 0, non-finite knobs,
  * strength/window/cap < 0, falloff <= 0, scale <= 0; H3_EUNSUPPORTED for a
- * dtype or head_dim outside the lists above; H3_EWORKSPACE; H3_ELAUNCH.
+ * dtype or head_dim outside the lists above, more than 65,535 heads, or bf16
+ * inputs with more than 8,388,608 keys (32-bit addressing of the transposed v
+ * copy); H3_EWORKSPACE; H3_ELAUNCH.
  */
 size_t attn_dense_tara_workspace(int nk, int heads, int head_dim, int dtype);
 int attn_dense_tara(const void* q, const void* k, const void* v, int dtype,

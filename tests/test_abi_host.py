@@ -116,8 +116,8 @@ def dense(**kw):
     ({"falloff": -1.0}, -1), ({"strength": -1.0}, -1), ({"cap": -0.5}, -1),
     ({"window": -0.1}, -1), ({"scale": 0.0}, -1), ({"scale": float("nan")}, -1),
     ({"d": 96}, -2), ({"d": 256}, -2), ({"dtype": 2}, -2), ({"odt": 5}, -2),
-    ({"heads": 70000}, -2),
-    ({}, -4), ({"ws": P, "wsb": 10}, -4),
+    ({"heads": 70000}, -2), ({"nk": (1 << 23) + 1}, -2),
+    ({}, -4), ({"ws": P, "wsb": 10}, -4), ({"nk": 1 << 23}, -4),
 ])
 def test_dense_argument_checks(kw, code):
     assert dense(**kw) == code
