@@ -88,8 +88,8 @@ struct RouterWs {
   int32_t* video;  // [nb]
   int32_t* counts; // [2]: n_prot, n_video
   float* vbar;     // [H][nb][D] (tail term only, else null)
-  uint16_t* wts;   // [H][nb][nbp] fp16 tail weights per (query block, video tile) (tail only)
-  uint16_t* vbt;   // [H][D][nbp] fp16 V means of the video tiles, transposed (tail only)
+  float* wts;      // [H][nb][nbp] tail weights per (query block, video tile) (tail only)
+  float* vbt;      // [H][D][nbp] V means of the video tiles, transposed (tail only)
   int nbp;         // nb rounded up to 32
 };
 // Tail term of the unrouted tiles (see router.hip); all pointers null when not wanted.
@@ -100,7 +100,7 @@ struct TailArgs {
   const float* vbar;   // [H][nb][D] block means of v
   float* lse;          // [H][nb] natural-log logit of the tail key
   float* v;            // [H][nb][D] value of the tail key
-  uint16_t* wts;       // [H][nb][nbp] fp16 normalised weights of the unrouted video tiles
+  float* wts;          // [H][nb][nbp] normalised weights of the unrouted video tiles
   int nbp;
 };
 size_t router_ws_bytes(int n, int H, int D, int bs, bool tail);

@@ -18,8 +18,8 @@
 // With the tail term ("H3 SLA Attention", inputs table, tail_correction) the pool pass
 // also takes the mean of V, and the top-k kernel folds the unrouted video tiles of each
 // query block into one pooled key: logit ln sum_u n_u exp(scale * S[qb,u]) from the same
-// float32 pooled scores, and normalised weights whose product with the V means (fp16 on
-// the matrix cores, float32 sums) gives the key's value.
+// float32 pooled scores, and normalised weights whose product with the V means (float32
+// on the matrix cores) gives the key's value.
 #include "h3_internal.h"
 
 #pragma clang fp contract(off)
@@ -342,28 +342,25 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
   }
   __syncthreads();
-  // normalised weights as fp16 rows [qb][nbp] (zero for routed tiles and past nv); the
-  // weighted V means are one matrix product per head (tail_v_kernel)
+  // normalised weights as float32 rows [qb][nbp] (zero for routed tiles and past nv);
+  // the weighted V means are one matrix product per head (tail_v_kernel)
   if (active && qb < nb) {
     const float* my_w = sc + w * nv;
     const float sm = tsum[w];
     const float inv = sm > 0.f ? 1.f / sm : 0.f;
-    uint16_t* row = tail.wts + ((int64_t)h * nb + qb) * tail.nbp;
-    for (int i = lane; i < tail.nbp; i += 64) {
-      const float wt = i < nv ? my_w[i] * inv : 0.f;
-      row[i] = __builtin_bit_cast(uint16_t, (_Float16)wt);
-    }
+    float* row = tail.wts + ((int64_t)h * nb + qb) * tail.nbp;
+    for (int i = lane; i < tail.nbp; i += 64) row[i] = i < nv ? my_w[i] * inv : 0.f;
   }
 }
 
-// fp16 V means of the video tiles, transposed: vbt[h][d][i] = vbar[h][video[i]][d] for
+// V means of the video tiles, transposed: vbt[h][d][i] = vbar[h][video[i]][d] for
 // i < n_video, zero up to nbp.
 template <int D>
 __global__ __launch_bounds__(256) void tail_vbar_kernel(const float* __restrict__ vbar,
                                                         const int32_t* __restrict__ video,
                                                         const int32_t* __restrict__ counts,
                                                         int nb, int nbp,
-                                                        uint16_t* __restrict__ vbt) {
+                                                        float* __restrict__ vbt) {
   const int h = blockIdx.y;
   const int i = blockIdx.x * 64 + (threadIdx.x & 63);
   const int nv = counts[1];
@@ -371,19 +368,20 @@ __global__ __launch_bounds__(256) void tail_vbar_kernel(const float* __restrict_
   const int kb = live ? video[i] : 0;
   for (int d = threadIdx.x >> 6; d < D; d += 4) {
     const float x = live ? vbar[((int64_t)h * nb + kb) * D + d] : 0.f;
-    if (i < nbp) vbt[((int64_t)h * D + d) * nbp + i] = __builtin_bit_cast(uint16_t, (_Float16)x);
+    if (i < nbp) vbt[((int64_t)h * D + d) * nbp + i] = x;
   }
 }
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // tail_v[h][qb][:] = sum_i wts[h][qb][i] * vbt[h][:][i]: a [nb x nv] x [nv x D] product per
-// head on the matrix cores (fp16 inputs, float32 sums). Workgroup = 32 query blocks of one
-// head; wave w takes the 32 output columns 32w..32w+31.
+// head on the matrix cores in float32 (v_mfma_f32_32x32x2_f32). Workgroup = 32 query
+// blocks of one head; wave w takes the 32 output columns 32w..32w+31. The k index of a
+// product step is a lane's own: lane half hh holds tiles k0 + 4hh + j for the four steps
+// j of a group of eight tiles, so that every lane reads its operands as float4.
 template <int D>
-__global__ __launch_bounds__(64 * (D / 32)) void tail_v_kernel(const uint16_t* __restrict__ wts,
-                                                               const uint16_t* __restrict__ vbt,
+__global__ __launch_bounds__(64 * (D / 32)) void tail_v_kernel(const float* __restrict__ wts,
+                                                               const float* __restrict__ vbt,
                                                                const int32_t* __restrict__ counts,
                                                                int nb, int nbp,
                                                                float* __restrict__ tail_v) {
@@ -391,16 +389,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void tail_v_kernel(const uint16_t* _
   const int qb0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kend = (counts[1] + 15) & ~15;  // video tiles, in steps of 16 (<= nbp)
+  const int kend = (counts[1] + 7) & ~7;  // video tiles, in steps of 8 (<= nbp)
   const bool row_ok = qb0 + l32 < nb;
-  const uint16_t* arow = wts + ((int64_t)h * nb + (row_ok ? qb0 + l32 : 0)) * nbp + 8 * hh;
-  const uint16_t* brow = vbt + ((int64_t)h * D + 32 * w + l32) * nbp + 8 * hh;
+  const float* arow = wts + ((int64_t)h * nb + (row_ok ? qb0 + l32 : 0)) * nbp + 4 * hh;
+  const float* brow = vbt + ((int64_t)h * D + 32 * w + l32) * nbp + 4 * hh;
   f32x16 acc = {};
-  for (int k0 = 0; k0 < kend; k0 += 16) {
-    f16x8 a = *(const f16x8*)(arow + k0);
-    if (!row_ok) a = f16x8{};
-    const f16x8 b = *(const f16x8*)(brow + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+  for (int k0 = 0; k0 < kend; k0 += 8) {
+    f32x4 a = *(const f32x4*)(arow + k0);
+    if (!row_ok) a = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 b = *(const f32x4*)(brow + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
   }
   // lane holds column 32w + l32 and rows 8(r/4) + 4hh + r%4
 #pragma unroll
@@ -420,7 +419,7 @@ size_t router_ws_bytes(int n, int H, int D, int bs, bool tail) {
   const size_t means = align256(nb * H * D * sizeof(float));
   size_t b = 2 * means + align256(nb * sizeof(int32_t)) + 256;
   if (tail)
-    b += means + align256((size_t)H * nb * nbp * 2) + align256((size_t)H * D * nbp * 2);
+    b += means + align256((size_t)H * nb * nbp * 4) + align256((size_t)H * D * nbp * 4);
   return b;
 }
 
@@ -444,9 +443,9 @@ RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
   if (tail) {
     w.vbar = (float*)p;
     p += means;
-    w.wts = (uint16_t*)p;
-    p += align256((size_t)H * nb * w.nbp * 2);
-    w.vbt = (uint16_t*)p;
+    w.wts = (float*)p;
+    p += align256((size_t)H * nb * w.nbp * 4);
+    w.vbt = (float*)p;
   }
   return w;
 }

@@ -233,10 +233,10 @@ def test_tail_entry_points_reject_bad_arguments():
     P = ctypes.c_void_p(16)
     nb = (1000 + 63) // 64
     nbp = (nb + 31) // 32 * 32
-    # plus the V means (float32), the fp16 weights [H][nb][nbp] and fp16 V^T means [H][d][nbp]
+    # plus the V means, the weights [H][nb][nbp] and the V^T means [H][d][nbp] (float32)
     assert (L.attn_block_router_tail_workspace(1000, 2, 64, 64)
             == L.attn_block_router_workspace(1000, 2, 64, 64) + _a256(nb * 2 * 64 * 4)
-            + _a256(2 * nb * nbp * 2) + _a256(2 * 64 * nbp * 2))
+            + _a256(2 * nb * nbp * 4) + _a256(2 * 64 * nbp * 4))
     base = [P, P, P, 1, 1000, 2, 64, P, 0, 64, 4, 0.125, P, P, 1, P, P]
     assert L.attn_block_router_tail(*base, None, 0, None) == -4
     for i, bad in ((2, None), (15, None), (16, None), (11, 0.0), (11, float("nan"))):

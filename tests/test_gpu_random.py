@@ -1,0 +1,114 @@
+"""Randomised GPU parity sweep.
+
+Each case draws a packed layout (spans of text, guide video, audio and output video in
+a random order, with random lengths and frame sizes, so tiles straddle frames and
+segments and the last block is ragged), a head count, head_dim, dtype, TARA knobs and a
+protected prefix, then checks against the float64 oracle:
+- dense TARA and the partition path, every output row;
+- the router (tile and protected lists bit-exact) and block-sparse attention at a random
+  block size and sparsity, with or without the tail term and audio sink blocks, every
+  output row;
+- for bf16 at block sizes 64 and 128, the int8 QK product against the oracle's int8
+  path.
+The seeds are fixed, so every run draws the same cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_02_amd import api, workloads as W
+from gpu_common import compare, f64, layout_device, to_device
+from test_gpu_small import _route_oracle, _tails_oracle
+from test_gpu_variants import _assemble
+
+pytestmark = pytest.mark.gpu
+
+KINDS = (W.SEG_TEXT, W.SEG_GUIDE, W.SEG_AUDIO, W.SEG_OUTPUT)
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(9000 + seed)
+    kinds = list(rng.permutation(KINDS)) + list(rng.choice(KINDS, size=int(rng.integers(0, 3))))
+    spans = []
+    for kind in kinds:
+        if kind in (W.SEG_GUIDE, W.SEG_OUTPUT):
+            frames = int(rng.integers(1, 7))
+            spans.append(W.Span(int(kind), frames * int(rng.integers(1, 150)), frames))
+        else:
+            spans.append(W.Span(int(kind), int(rng.integers(1, 200))))
+    n = sum(s.length for s in spans)
+    dtype = str(rng.choice(["bf16", "f32"]))
+    params = dict(strength=float(rng.choice([0.0, 0.5, 2.0, 7.0])),
+                  window=float(rng.choice([0.0, 0.2, 0.5])),
+                  falloff=float(rng.choice([0.1, 0.25, 1.0])),
+                  cap=float(rng.choice([0.5, 6.0, 20.0])))
+    wl = W.custom(f"random_{seed}", spans, heads=int(rng.integers(1, 4)),
+                  head_dim=int(rng.choice([64, 128])), dtype=dtype, seed_index=200 + seed,
+                  frame_weight=float(rng.choice([0.0, 0.7])),
+                  protected_prefix_len=int(rng.integers(0, min(n, 300) + 1)), **params)
+    sparse = dict(bs=int(rng.choice([32, 64, 128])), sparsity=float(rng.choice([0.0, 0.3, 0.8, 0.95])),
+                  tail=bool(rng.integers(0, 2)), sinks=bool(rng.integers(0, 2)),
+                  int8=bool(rng.integers(0, 2)))
+    return wl, sparse
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_layouts(seed):
+    wl, sp = _random_case(seed)
+    dtype, H, d, bs = wl.dtype, wl.heads, wl.head_dim, sp["bs"]
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    q64, k64, v64 = f64(q, dtype), f64(k, dtype), f64(v, dtype)
+    print(f"case {wl.name} n={wl.n} spans={[(s.seg, s.length, s.frames) for s in wl.spans]} "
+          f"H={H} d={d} {dtype} tara={wl.tara} prefix={wl.protected_prefix_len} {sp}",
+          flush=True)
+
+    # dense and the partition path
+    o_ref, l_ref = oracle.dense_tara(q64, k64, v64, seg, t, seg, t, wl.tara, wl.scale)
+    o, lse = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} dense")
+    o, lse = api.attn_dense_tara_via(qd, kd, vd, seg_d, t_d, seg, t, *wl.tara, scale=wl.scale)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} via")
+
+    # router and block-sparse attention
+    prefix = wl.protected_prefix_len
+    plan = api.router_plan(seg, prefix, sp["sparsity"], block_size=bs)
+    _, prot_ref, _, k_ref = oracle.router_plan(seg, prefix, bs, sp["sparsity"])
+    assert plan["k_sel"] == k_ref and plan["n_prot"] == len(prot_ref)
+    if sp["tail"]:
+        tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, prefix, plan["k_sel"],
+                                                         plan["n_prot"], scale=wl.scale,
+                                                         block_size=bs)
+    else:
+        tiles, prot = api.attn_block_router(qd, kd, seg_d, prefix, plan["k_sel"],
+                                            plan["n_prot"], block_size=bs)
+        tl = tv = None
+    sinks = (1 << W.SEG_AUDIO) if sp["sinks"] else 0
+    o, lse = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, sinks, tl, tv,
+                                         *wl.tara, scale=wl.scale, block_size=bs)
+    torch.cuda.synchronize()
+    tiles_np = tiles.cpu().numpy()
+    assert np.array_equal(prot.cpu().numpy(), prot_ref)
+    assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(H), bs=bs))
+    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(H), bs=bs) if sp["tail"] else None
+    sink_segs = (W.SEG_AUDIO,) if sp["sinks"] else ()
+    ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, bs, prot_ref, tiles_np,
+                              tails=tails, sink_segments=sink_segs)
+    o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} sparse")
+
+    # int8 QK product (bf16 inputs, block sizes 64 and 128)
+    if sp["int8"] and dtype == "bf16" and bs != 32:
+        o, lse = api.attn_block_sparse_int8qk(qd, kd, vd, seg_d, t_d, tiles, prot, tail_lse=tl,
+                                              tail_v=tv, sink_segments=sinks,
+                                              strength=wl.strength, window=wl.window,
+                                              falloff=wl.falloff, cap=wl.cap, scale=wl.scale,
+                                              block_size=bs)
+        torch.cuda.synchronize()
+        ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, bs, prot_ref,
+                                  tiles_np, tails=tails, sink_segments=sink_segs, int8_qk=True)
+        o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
+        compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} int8")
