@@ -10,6 +10,9 @@ protected prefix, then checks against the float64 oracle:
   output row;
 - for bf16 at block sizes 64 and 128, the int8 QK product against the oracle's int8
   path.
+A second set of cases takes the knobs to their extremes (protected prefixes 0 and n,
+sparsity 0.99, strength up to 50 and cap up to 60, falloff 0.01, a second softmax scale)
+and also feeds hand-built tile lists with repeated, negative and out-of-range entries.
 The seeds are fixed, so every run draws the same cases."""
 import numpy as np
 import pytest
@@ -112,3 +115,89 @@ def test_random_layouts(seed):
                                   tiles_np, tails=tails, sink_segments=sink_segs, int8_qk=True)
         o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
         compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} int8")
+
+
+def _extreme_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    kinds = list(rng.permutation(KINDS)) + list(rng.choice(KINDS, size=int(rng.integers(0, 3))))
+    spans = []
+    for kind in kinds:
+        if kind in (W.SEG_GUIDE, W.SEG_OUTPUT):
+            frames = int(rng.integers(1, 9))
+            spans.append(W.Span(int(kind), frames * int(rng.integers(1, 200)), frames))
+        else:
+            spans.append(W.Span(int(kind), int(rng.integers(1, 300))))
+    n = sum(s.length for s in spans)
+    prefix = int(rng.choice([0, n, int(rng.integers(0, n + 1))]))
+    wl = W.custom(f"extreme_{seed}", spans, heads=int(rng.integers(1, 4)),
+                  head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+                  seed_index=300 + seed, frame_weight=float(rng.choice([0.0, 0.7, 0.95])),
+                  qk_gain=float(rng.choice([0.5, 1.0])), protected_prefix_len=prefix,
+                  strength=float(rng.choice([0.0, 0.01, 50.0])),
+                  window=float(rng.choice([0.0, 3.0])), falloff=float(rng.choice([0.01, 10.0])),
+                  cap=float(rng.choice([0.0, 0.5, 60.0])))
+    scale = float(rng.choice([wl.scale, 0.05]))
+    return wl, scale, dict(bs=int(rng.choice([32, 64, 128])), sparsity=float(rng.choice([0.5, 0.99])),
+                           tail=bool(rng.integers(0, 2)), sinks=bool(rng.integers(0, 2)),
+                           hand=bool(rng.integers(0, 2))), rng
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_extremes(seed):
+    """Protected prefixes 0 and n, sparsity 0.99, extreme TARA knobs (strength 0.01-50,
+    cap 0-60, falloff 0.01-10, window 3 s), a second scale, and hand-built tile lists with
+    repeats, -1 and out-of-range entries (a row with no key at all gives o = 0 and
+    L = -inf on both sides)."""
+    wl, scale, sp, rng = _extreme_case(seed)
+    dtype, H, d, bs = wl.dtype, wl.heads, wl.head_dim, sp["bs"]
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, dtype) for x in (q, k, v))
+    q64, k64, v64 = f64(q, dtype), f64(k, dtype), f64(v, dtype)
+    print(f"case {wl.name} n={wl.n} H={H} d={d} {dtype} tara={wl.tara} scale={scale:.4g} "
+          f"prefix={wl.protected_prefix_len} {sp}", flush=True)
+    o_ref, l_ref = oracle.dense_tara(q64, k64, v64, seg, t, seg, t, wl.tara, scale)
+    o, lse = api.attn_dense_tara(qd, kd, vd, seg_d, t_d, seg_d, t_d, *wl.tara, scale=scale)
+    torch.cuda.synchronize()
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} dense")
+
+    prefix, nb = wl.protected_prefix_len, (wl.n + bs - 1) // bs
+    tl = tv = tails = None
+    if sp["hand"]:
+        k_sel = int(rng.integers(1, 12))
+        tiles_np = rng.integers(-2, nb + 3, size=(H, nb, k_sel)).astype(np.int32)
+        prot_np = rng.integers(-1, nb + 2, size=int(rng.integers(0, 5))).astype(np.int32)
+        tiles, prot = torch.from_numpy(tiles_np).cuda(), torch.from_numpy(prot_np).cuda()
+    else:
+        plan = api.router_plan(seg, prefix, sp["sparsity"], block_size=bs)
+        if sp["tail"]:
+            tiles, prot, tl, tv = api.attn_block_router_tail(qd, kd, vd, seg_d, prefix,
+                                                             plan["k_sel"], plan["n_prot"],
+                                                             scale=scale, block_size=bs)
+        else:
+            tiles, prot = api.attn_block_router(qd, kd, seg_d, prefix, plan["k_sel"],
+                                                plan["n_prot"], block_size=bs)
+        torch.cuda.synchronize()
+        tiles_np, prot_np = tiles.cpu().numpy(), prot.cpu().numpy()
+        _, prot_ref, _, _ = oracle.router_plan(seg, prefix, bs, sp["sparsity"])
+        assert np.array_equal(prot_np, prot_ref)
+        assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(H),
+                                                       bs=bs))
+        if sp["tail"]:
+            tails = {h: oracle.tail_terms(W.to_float32(q[:, h], dtype), W.to_float32(k[:, h], dtype),
+                                          v64[:, h], seg, prefix, bs, tiles_np[h], scale)
+                     for h in range(H)}
+    sinks = (1 << W.SEG_AUDIO) if sp["sinks"] else 0
+    o, lse = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, sinks, tl, tv,
+                                         *wl.tara, scale=scale, block_size=bs)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, scale, bs, prot_np, tiles_np,
+                              tails=tails, sink_segments=(W.SEG_AUDIO,) if sp["sinks"] else ())
+    o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse.cpu().numpy()), empty)
+    if empty.any():
+        assert np.all(o.float().cpu().numpy()[empty] == 0)
+        l_ref = np.where(empty, 0.0, l_ref)
+        lse = torch.where(torch.isneginf(lse), torch.zeros_like(lse), lse)
+    compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} sparse")
