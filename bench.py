@@ -103,6 +103,9 @@ def _counter_kib(path, counter, kernel_substr):
     return float(np.mean(vals)), len(vals)
 
 
+DENSE_ONLY = "python3 bench.py --only dense --steps 1 --warmup 0 --no-cpu --no-sweep"
+
+
 def pmc_summary(dirs):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
     kern = DENSE_KERNEL
@@ -123,16 +126,13 @@ def pmc_summary(dirs):
            "hbm_bytes_per_launch": fetch + write,
            "launches_averaged": [nf, nw],
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
-               "python3 bench.py --only dense --steps 1 --warmup 0 --no-cpu --no-sweep",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
-               "python3 bench.py --only dense --steps 1 --warmup 0 --no-cpu --no-sweep",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_cfetch -o run -- "
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- {DENSE_ONLY}",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- {DENSE_ONLY}",
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o run -- "
                "python3 bench.py --copy-calibration",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_cwrite -o run -- "
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o run -- "
                "python3 bench.py --copy-calibration",
-               "python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write "
-               "gpurun_out/pmc_cfetch gpurun_out/pmc_cwrite"]}
+               f"python3 bench.py --pmc-summary {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir}"]}
     with open(PMC_SUMMARY, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))

@@ -1,8 +1,8 @@
 // Pooled block router for block-sparse attention.
 //
-// "H3 SLA Attention", "How it works": every query block is scored against every key
-// block by one small pooled Q/K product, and only the best (1 - sparsity) share is
-// attended; inputs table: blocks overlapping language or audio rows are always attended.
+// "H3 SLA Attention", "How it works": a single product of the block-mean queries with
+// the block-mean keys rates each (query block, key block) pair, and a query block keeps
+// the highest-rated (1 - sparsity) share of the key blocks; inputs table: blocks overlapping language or audio rows are always attended.
 // "H3 sparse-attention breakpoints": the density is a fraction of the video KV tiles.
 //
 // Three kernels, all deterministic (no floating-point atomics):

@@ -118,9 +118,9 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
 
 /*
  * Pooled block router.
- * From "H3 SLA Attention", "How it works": every query block is scored
- * against every key block by one pooled Q/K product and keeps its top k video
- * tiles. Per head: qbar_b, kbar_b = mean of the block's valid rows (float32
+ * From "H3 SLA Attention", "How it works": one product of block-mean queries
+ * with block-mean keys rates all (query block, key block) pairs; each query
+ * block keeps its k highest-rated video tiles. Per head: qbar_b, kbar_b = mean of the block's valid rows (float32
  * sums in row order from +0.0, then a correctly rounded division by the row
  * count); score(qb, kb) = sum over d = 0..head_dim-1 of fl32(qbar[d] *
  * kbar[d]) added in order, no fused multiply-add, unscaled, over video tiles
@@ -173,9 +173,9 @@ int attn_block_sparse(const void* q, const void* k, const void* v, int dtype,
 
 /*
  * Routing with the pooled tail term.
- * From "H3 SLA Attention", inputs table (tail_correction): instead of a hard
- * zero for the video tiles the top-k leaves out, one pooled term stands in for
- * all of them, scored from the pooled centroids the selection already computes.
+ * From "H3 SLA Attention", inputs table (tail_correction): rather than dropping
+ * the video tiles the top-k leaves out, one pooled term stands in for
+ * all of them; its score reuses the block means that routing has formed.
  * Reading (the page gives no formula): for query block qb of head h and its
  * unrouted video tiles U,
  *   tail_lse[h][qb] = ln sum_{u in U} n_u * exp(scale * S[qb][u]),

@@ -2,9 +2,9 @@
 only).
 
 Source (web page): "H3 SLA Attention", inputs table, use_int8_qk: Q and K are
-quantized to int8 per token with a dynamic scale before the QK dot product on the
-attended blocks, and the PV product stays in full precision (the split of an int8
-QK product with a 16-bit PV product).
+rounded to int8 row by row, each row with a scale computed from its own values, and
+only then multiplied on the attended blocks; the PV product keeps full precision (an
+int8 QK product next to a 16-bit PV product).
 
 Reading (the page gives no formula). For each (row, head) vector x of head_dim
 float32 values, in float32 arithmetic with correct rounding:

@@ -1,16 +1,16 @@
 """Pooled block routing for block-sparse attention (test infrastructure only).
 
 Sources (web pages):
-- "H3 SLA Attention" node page, "How it works": each query block is scored
-  against every key block by one small pooled matmul, and only the top
-  (1 - sparsity_ratio) fraction is attended; nothing is trained, the choice is
-  made at run time from Q and K.
+- "H3 SLA Attention" node page, "How it works": one small product of block-mean
+  queries with block-mean keys rates every (query block, key block) pair, and a
+  query block attends only its best-rated (1 - sparsity_ratio) share of key
+  blocks; no weights are learned, the choice comes from Q and K at run time.
 - same page, "The inputs that matter" and the inputs table: sparsity_ratio is
   the fraction of key blocks skipped and 0.0 disables sparsity; block_size 64;
-  protect_audio always attends the [text | cond | audio] prefix, i.e. blocks
-  overlapping language tokens and audio segments.
+  with protect_audio, the blocks that hold language tokens or audio segments (the
+  [text | cond | audio] part of the sequence) are attended by every query block.
 - "H3 sparse-attention breakpoints" page: the density is a fraction of the
-  video key/value tiles; text and audio context are not reduced.
+  video key/value tiles, while the text and audio context stays whole.
 
 Readings where the pages are silent (each listed in the design notes):
 - pooled vector = mean of the block's valid rows, accumulated in float32 in

@@ -5,9 +5,9 @@ Sources (web pages):
   each query block attends only its selected key blocks plus the protected
   [text | cond | audio] blocks; unselected blocks get a hard zero.
 - same page, inputs table, tail_correction (off by default): instead of the
-  hard zero, one pooled term stands in for every key block the top-k left out,
-  scored from the pooled centroids the selection already computes, at the cost
-  of one more mean-pool of V and a small reduction.
+  hard zero, one pooled term stands in for every key block the top-k left out;
+  its score reuses the routing's block means, so the extra work is a block mean
+  of V and a small reduction.
 - "Flash Partitions for H3 native temporal alignment", section 1: the same
   score rule as dense TARA inside the attended tiles.
 
@@ -26,9 +26,9 @@ selection; halving it doubles the block count and keeps the attention work).
 Query blocks and key blocks have the same size.
 
 Sink queries ("Per-layer attention config LoRAs", section "Experimental:
-audio/text protection": the audio queries are kept fully exact, sink_queries =
-audio): a query block holding any row of a sink segment attends every key of the
-sequence. Reading: the whole block is dense,
+audio/text protection": with sink_queries = audio, attention of the audio
+queries is computed without sparsity): a query block holding any row of a sink
+segment attends every key of the sequence. Reading: the whole block is dense,
 including its few non-sink rows at a segment boundary, and it has no tail term
 since nothing is left out.
 """
