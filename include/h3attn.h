@@ -120,11 +120,11 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
  * Pooled block router.
  * From "H3 SLA Attention", "How it works": one product of block-mean queries
  * with block-mean keys rates all (query block, key block) pairs; each query
- * block keeps its k highest-rated video tiles. Per head: qbar_b, kbar_b = mean of the block's valid rows (float32
- * sums in row order from +0.0, then a correctly rounded division by the row
- * count); score(qb, kb) = sum over d = 0..head_dim-1 of fl32(qbar[d] *
- * kbar[d]) added in order, no fused multiply-add, unscaled, over video tiles
- * kb only; the k_sel highest scores are kept (ties to the lower block index,
+ * block keeps its k highest-rated video tiles. Per head: qbar_b, kbar_b = mean
+ * of the block's valid rows (float32 sums in row order from +0.0, then a
+ * correctly rounded division by the row count); score(qb, kb) = sum over
+ * d = 0..head_dim-1 of fl32(qbar[d] * kbar[d]) added in order, no fused
+ * multiply-add, unscaled, over video tiles kb only; the k_sel highest scores are kept (ties to the lower block index,
  * NaN last) and written in ascending block order. Every query block is
  * routed, text and audio blocks included.
  * tiles: device int32 [heads][nb][k_sel], nb = ceil(n / block_size); entries
@@ -152,9 +152,9 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
  * else (a hard zero, no tail term). Blocks are block_size rows; tiles is
  * [heads][ceil(n / block_size)][k_sel]. Entries outside [0, ceil(n /
  * block_size)) are skipped and a block listed more than once counts once.
- * Inside those tiles the
- * score is the dense TARA score of attn_dense_tara, so the penalty applies to
- * routed guide tiles of output-video queries when strength > 0 and cap > 0.
+ * Inside those tiles the score is the dense TARA score of attn_dense_tara, so
+ * the penalty applies to routed guide tiles of output-video queries when
+ * strength > 0 and cap > 0.
  * Workspace: attn_block_sparse_workspace(n, heads, head_dim, dtype) bytes.
  * Errors: as attn_dense_tara, plus H3_EINVAL for k_sel < 0, n_prot < 0,
  * n_prot + k_sel == 0, null tiles (k_sel > 0) or prot (n_prot > 0);
@@ -219,7 +219,7 @@ int attn_block_sparse_tail(const void* q, const void* k, const void* v, int dtyp
 /*
  * Block-sparse attention with sink query blocks.
  * From "Per-layer attention config LoRAs", section "Experimental: audio/text
- * protection": the audio queries are kept fully exact (sink_queries = audio).
+ * protection": with sink_queries = audio, the audio queries see no sparsity.
  * attn_block_sparse, where a query block holding any row whose segment id s
  * has bit s set in sink_segments attends every key of the sequence (its list
  * is not read, and it takes no tail term: nothing is left out). The whole
