@@ -17,7 +17,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libh3attn.so")
 
-H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE = 0, -1, -2, -3, -4
+H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE, H3_ENOMEM = 0, -1, -2, -3, -4, -5
 H3_DTYPE_F32, H3_DTYPE_BF16 = 0, 1
 
 EXPORTS = (

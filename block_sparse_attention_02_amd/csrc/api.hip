@@ -3,6 +3,7 @@
 //
 // Every check runs before the first HIP call, so a rejected call never touches the
 // device. Kernels run on the caller's stream; nothing here synchronises.
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -182,6 +183,18 @@ ViaPlan make_plan(const uint8_t* seg, const float* t, int n, int heads, int head
   return p;
 }
 
+// make_plan without exceptions: false when host memory for the plan cannot be allocated
+// (no exception may cross the C boundary).
+bool plan_nothrow(const uint8_t* seg, const float* t, int n, int heads, int head_dim, int dtype,
+                  ViaPlan& out) noexcept {
+  try {
+    out = make_plan(seg, t, n, heads, head_dim, dtype);
+    return true;
+  } catch (...) {
+    return false;
+  }
+}
+
 int vt_slot(const ViaPlan& p, int a, int b) {
   for (size_t i = 0; i < p.vt_ranges.size(); ++i)
     if (p.vt_ranges[i].a == a && p.vt_ranges[i].b == b) return (int)i;
@@ -206,6 +219,7 @@ const char* h3attn_status_string(int status) {
     case H3_EUNSUPPORTED: return "unsupported dtype, head_dim or block_size";
     case H3_ELAUNCH: return "kernel launch failed";
     case H3_EWORKSPACE: return "workspace missing or too small";
+    case H3_ENOMEM: return "host memory for the call plan could not be allocated";
     default: return "unknown status";
   }
 }
@@ -459,7 +473,8 @@ size_t attn_dense_tara_via_workspace(const uint8_t* seg_host, const float* t_hos
                                      int heads, int head_dim, int dtype) {
   if (!seg_host || !t_host || n <= 0 || heads <= 0 || !dim_ok(head_dim) || !dtype_ok(dtype))
     return 0;
-  return make_plan(seg_host, t_host, n, heads, head_dim, dtype).total;
+  ViaPlan p;
+  return plan_nothrow(seg_host, t_host, n, heads, head_dim, dtype, p) ? p.total : 0;
 }
 
 int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, int n, int heads,
@@ -473,7 +488,8 @@ int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, 
   if (!dtype_ok(dtype) || !dtype_ok(o_dtype) || !dim_ok(head_dim) || heads > 65535)
     return H3_EUNSUPPORTED;
   if (dtype == H3_DTYPE_BF16 && n > kMaxBf16Keys) return H3_EUNSUPPORTED;
-  const ViaPlan p = make_plan(seg_host, t_host, n, heads, head_dim, dtype);
+  ViaPlan p;
+  if (!plan_nothrow(seg_host, t_host, n, heads, head_dim, dtype, p)) return H3_ENOMEM;
   if (!ws || ws_bytes < p.total) return H3_EWORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;

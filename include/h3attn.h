@@ -41,6 +41,7 @@ extern "C" {
 #define H3_EUNSUPPORTED (-2)  /* dtype, head_dim not in {64,128}, block_size not in {32,64,128} */
 #define H3_ELAUNCH      (-3)  /* a kernel launch failed (hipGetLastError) */
 #define H3_EWORKSPACE   (-4)  /* workspace pointer null or smaller than required */
+#define H3_ENOMEM       (-5)  /* host memory for a call's plan could not be allocated */
 
 #define H3_DTYPE_F32  0
 #define H3_DTYPE_BF16 1
@@ -316,7 +317,9 @@ int partition_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const fl
  * up to rounding order. Self-attention only (q, k, v share the n rows).
  * seg_host/t_host: host copies of seg/t (used to plan the calls).
  * Workspace: attn_dense_tara_via_workspace(seg_host, t_host, n, heads,
- * head_dim, dtype) bytes. Errors: as attn_dense_tara.
+ * head_dim, dtype) bytes (0 for invalid arguments or when the plan cannot be
+ * built). Errors: as attn_dense_tara, plus H3_ENOMEM when host memory for the
+ * plan of calls cannot be allocated.
  */
 size_t attn_dense_tara_via_workspace(const uint8_t* seg_host, const float* t_host, int n,
                                      int heads, int head_dim, int dtype);

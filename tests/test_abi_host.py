@@ -43,6 +43,8 @@ def test_version_and_status_strings():
     assert api.status_string(0) == "ok"
     assert "invalid" in api.status_string(-1)
     assert "workspace" in api.status_string(-4)
+    assert "host memory" in api.status_string(api.H3_ENOMEM)
+    assert api.status_string(-6) == "unknown status"
 
 
 def test_missing_library_fails_loudly(monkeypatch):
