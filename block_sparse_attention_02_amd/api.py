@@ -124,10 +124,47 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _contig(*ts):
-    for t in ts:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+def _expect(func, name, t, shape, dtypes, device):
+    """Checks one tensor argument before its pointer is handed to the library: a
+    contiguous tensor on ``device`` with the given shape (None entries are free) and a
+    dtype in ``dtypes``. A wrong buffer would otherwise be read or written out of range
+    on the GPU."""
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{func}: {name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{func}: {name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{func}: {name} has dtype {t.dtype}, expected one of {dtypes}")
+    if len(t.shape) != len(shape) or any(w is not None and g != w
+                                         for g, w in zip(t.shape, shape)):
+        raise ValueError(f"{func}: {name} has shape {tuple(t.shape)}, expected "
+                         f"{tuple('*' if w is None else w for w in shape)}")
+
+
+def _check_args(func, q, spec, ws=None):
+    """Validates q (a [rows, heads, head_dim] bf16 or float32 tensor on the current GPU)
+    and then every (name, tensor, shape, dtypes) of ``spec`` against q's device; the
+    workspace may have any dtype."""
+    import torch
+    if not q.is_cuda or q.device.index != torch.cuda.current_device():
+        raise ValueError(f"{func}: tensors must be on the current GPU, q is on {q.device}")
+    _expect(func, "q", q, (None, None, None), (torch.bfloat16, torch.float32), q.device)
+    for name, t, shape, dtypes in spec:
+        _expect(func, name, t, shape, dtypes, q.device)
+    if ws is not None:
+        _expect(func, "ws", ws, (None,) * ws.dim(), (ws.dtype,), q.device)
+
+
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _dt():
+    import torch
+    return {"f32": (torch.float32,), "bf16f32": (torch.bfloat16, torch.float32),
+            "u8": (torch.uint8,), "i32": (torch.int32,), "i8": (torch.int8,)}
 
 
 def _empty_like_out(q, o_dtype):
@@ -165,12 +202,17 @@ def attn_dense_tara(q, k, v, q_seg, q_t, k_seg, k_t, strength=2.0, window=0.20, 
     need = dense_tara_workspace_bytes(nk, H, D, dt)
     if ws is None:
         ws = _workspace(need, q.device)
-    _contig(q, k, v, q_seg, q_t, k_seg, k_t, o, lse)
+    T = _dt()
+    _check_args("attn_dense_tara", q, [
+        ("k", k, (nk, H, D), (q.dtype,)), ("v", v, (nk, H, D), (q.dtype,)),
+        ("q_seg", q_seg, (nq,), T["u8"]), ("q_t", q_t, (nq,), T["f32"]),
+        ("k_seg", k_seg, (nk,), T["u8"]), ("k_t", k_t, (nk,), T["f32"]),
+        ("o", o, (nq, H, D), T["bf16f32"]), ("lse", lse, (nq, H), T["f32"])], ws)
     st = lib().attn_dense_tara(_ptr(q), _ptr(k), _ptr(v), dt, nq, nk, H, D,
                                _ptr(q_seg), _ptr(q_t), _ptr(k_seg), _ptr(k_t),
                                strength, window, falloff, cap, scale,
                                _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
-                               0 if ws is None else ws.numel(), _stream(stream))
+                               _nbytes(ws), _stream(stream))
     _check("attn_dense_tara", st)
     return o, lse
 
@@ -203,12 +245,15 @@ def attn_block_router(q, k, seg, protected_prefix_len, k_sel, n_prot, block_size
         prot = torch.empty((n_prot,), dtype=torch.int32, device=q.device)
     if ws is None:
         ws = _workspace(router_workspace_bytes(n, H, D, block_size), q.device)
-    _contig(q, k, seg, tiles, prot)
+    T = _dt()
+    _check_args("attn_block_router", q, [
+        ("k", k, (n, H, D), (q.dtype,)), ("seg", seg, (n,), T["u8"]),
+        ("tiles", tiles, (H, nb, k_sel), T["i32"]), ("prot", prot, (n_prot,), T["i32"])], ws)
     st = lib().attn_block_router(_ptr(q), _ptr(k), _dtype_code(q), n, H, D, _ptr(seg),
                                  protected_prefix_len, block_size, k_sel,
                                  _ptr(tiles) if k_sel > 0 else None,
                                  _ptr(prot) if n_prot > 0 else None, n_prot,
-                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                                 _ptr(ws), _nbytes(ws), _stream(stream))
     _check("attn_block_router", st)
     return tiles, prot
 
@@ -237,13 +282,18 @@ def attn_block_router_tail(q, k, v, seg, protected_prefix_len, k_sel, n_prot, sc
         tail_v = torch.empty((H, nb, D), dtype=torch.float32, device=q.device)
     if ws is None:
         ws = _workspace(router_tail_workspace_bytes(n, H, D, block_size), q.device)
-    _contig(q, k, v, seg, tiles, prot, tail_lse, tail_v)
+    T = _dt()
+    _check_args("attn_block_router_tail", q, [
+        ("k", k, (n, H, D), (q.dtype,)), ("v", v, (n, H, D), (q.dtype,)),
+        ("seg", seg, (n,), T["u8"]), ("tiles", tiles, (H, nb, k_sel), T["i32"]),
+        ("prot", prot, (n_prot,), T["i32"]), ("tail_lse", tail_lse, (H, nb), T["f32"]),
+        ("tail_v", tail_v, (H, nb, D), T["f32"])], ws)
     st = lib().attn_block_router_tail(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), n, H, D,
                                       _ptr(seg), protected_prefix_len, block_size, k_sel, scale,
                                       _ptr(tiles) if k_sel > 0 else None,
                                       _ptr(prot) if n_prot > 0 else None, n_prot,
                                       _ptr(tail_lse), _ptr(tail_v), _ptr(ws),
-                                      0 if ws is None else ws.numel(), _stream(stream))
+                                      _nbytes(ws), _stream(stream))
     _check("attn_block_router_tail", st)
     return tiles, prot, tail_lse, tail_v
 
@@ -265,13 +315,14 @@ def attn_block_sparse(q, k, v, seg, t, tiles, prot, strength=2.0, window=0.20, f
         scale = 1.0 / float(np.sqrt(D))
     if ws is None:
         ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
-    _contig(q, k, v, seg, t, tiles, prot, o, lse)
+    _check_args("attn_block_sparse", q, _sparse_spec(q, k, v, seg, t, tiles, prot, None, None,
+                                                     o, lse, block_size), ws)
     st = lib().attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
                                  strength, window, falloff, cap, scale, block_size,
                                  _ptr(tiles) if k_sel > 0 else None, k_sel,
                                  _ptr(prot) if n_prot > 0 else None, n_prot,
                                  _ptr(o), _dtype_code(o), _ptr(lse), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(stream))
+                                 _nbytes(ws), _stream(stream))
     _check("attn_block_sparse", st)
     return o, lse
 
@@ -293,13 +344,15 @@ def attn_block_sparse_tail(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, stren
         scale = 1.0 / float(np.sqrt(D))
     if ws is None:
         ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
-    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    _check_args("attn_block_sparse_tail", q, _sparse_spec(q, k, v, seg, t, tiles, prot,
+                                                          tail_lse, tail_v, o, lse, block_size),
+                ws)
     st = lib().attn_block_sparse_tail(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
                                       strength, window, falloff, cap, scale, block_size,
                                       _ptr(tiles) if k_sel > 0 else None, k_sel,
                                       _ptr(prot) if n_prot > 0 else None, n_prot,
                                       _ptr(tail_lse), _ptr(tail_v), _ptr(o), _dtype_code(o),
-                                      _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _ptr(lse), _ptr(ws), _nbytes(ws),
                                       _stream(stream))
     _check("attn_block_sparse_tail", st)
     return o, lse
@@ -324,7 +377,9 @@ def attn_block_sparse_sinks(q, k, v, seg, t, tiles, prot, sink_segments, tail_ls
         scale = 1.0 / float(np.sqrt(D))
     if ws is None:
         ws = _workspace(lib().attn_block_sparse_workspace(n, H, D, dt), q.device)
-    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    _check_args("attn_block_sparse_sinks", q, _sparse_spec(q, k, v, seg, t, tiles, prot,
+                                                           tail_lse, tail_v, o, lse, block_size),
+                ws)
     st = lib().attn_block_sparse_sinks(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg),
                                        _ptr(t), strength, window, falloff, cap, scale, block_size,
                                        _ptr(tiles) if k_sel > 0 else None, k_sel,
@@ -332,9 +387,20 @@ def attn_block_sparse_sinks(q, k, v, seg, t, tiles, prot, sink_segments, tail_ls
                                        _ptr(tail_lse) if tail_lse is not None else None,
                                        _ptr(tail_v) if tail_v is not None else None,
                                        int(sink_segments), _ptr(o), _dtype_code(o), _ptr(lse),
-                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                                       _ptr(ws), _nbytes(ws), _stream(stream))
     _check("attn_block_sparse_sinks", st)
     return o, lse
+
+
+def _sparse_spec(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse, block_size):
+    n, H, D = q.shape
+    nb = (n + block_size - 1) // block_size
+    T = _dt()
+    return [("k", k, (n, H, D), (q.dtype,)), ("v", v, (n, H, D), (q.dtype,)),
+            ("seg", seg, (n,), T["u8"]), ("t", t, (n,), T["f32"]),
+            ("tiles", tiles, (H, nb, None), T["i32"]), ("prot", prot, (None,), T["i32"]),
+            ("tail_lse", tail_lse, (H, nb), T["f32"]), ("tail_v", tail_v, (H, nb, D), T["f32"]),
+            ("o", o, (n, H, D), T["bf16f32"]), ("lse", lse, (n, H), T["f32"])]
 
 
 def quantize_int8(x, x8=None, scales=None, stream=None):
@@ -345,7 +411,9 @@ def quantize_int8(x, x8=None, scales=None, stream=None):
         x8 = torch.empty((n, H, D), dtype=torch.int8, device=x.device)
     if scales is None:
         scales = torch.empty((n, H), dtype=torch.float32, device=x.device)
-    _contig(x, x8, scales)
+    T = _dt()
+    _check_args("attn_quantize_int8", x, [("x8", x8, (n, H, D), T["i8"]),
+                                          ("scales", scales, (n, H), T["f32"])])
     st = lib().attn_quantize_int8(_ptr(x), _dtype_code(x), n, H, D, _ptr(x8), _ptr(scales),
                                   _stream(stream))
     _check("attn_quantize_int8", st)
@@ -374,7 +442,9 @@ def attn_block_sparse_int8qk(q, k, v, seg, t, tiles, prot, tail_lse=None, tail_v
         scale = 1.0 / float(np.sqrt(D))
     if ws is None:
         ws = _workspace(int8qk_workspace_bytes(n, H, D), q.device)
-    _contig(q, k, v, seg, t, tiles, prot, tail_lse, tail_v, o, lse)
+    _check_args("attn_block_sparse_int8qk", q, _sparse_spec(q, k, v, seg, t, tiles, prot,
+                                                            tail_lse, tail_v, o, lse,
+                                                            block_size), ws)
     st = lib().attn_block_sparse_int8qk(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg),
                                         _ptr(t), strength, window, falloff, cap, scale,
                                         block_size, _ptr(tiles) if k_sel > 0 else None, k_sel,
@@ -382,7 +452,7 @@ def attn_block_sparse_int8qk(q, k, v, seg, t, tiles, prot, tail_lse=None, tail_v
                                         _ptr(tail_lse) if tail_lse is not None else None,
                                         _ptr(tail_v) if tail_v is not None else None,
                                         int(sink_segments), _ptr(o), _dtype_code(o), _ptr(lse),
-                                        _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _ptr(ws), _nbytes(ws),
                                         _stream(stream))
     _check("attn_block_sparse_int8qk", st)
     return o, lse
@@ -391,7 +461,11 @@ def attn_block_sparse_int8qk(q, k, v, seg, t, tiles, prot, tail_lse=None, tail_v
 def partition_lse_merge(o_acc, lse_acc, o_i, lse_i, log_w=0.0, log_w_rows=None, stream=None):
     """In-place stable LSE merge of (o_i, lse_i) into (o_acc, lse_acc)."""
     rows, H, D = o_acc.shape
-    _contig(o_acc, lse_acc, o_i, lse_i, log_w_rows)
+    T = _dt()
+    _check_args("partition_lse_merge", o_acc, [
+        ("o_acc", o_acc, (rows, H, D), T["f32"]), ("lse_acc", lse_acc, (rows, H), T["f32"]),
+        ("o_i", o_i, (rows, H, D), T["f32"]), ("lse_i", lse_i, (rows, H), T["f32"]),
+        ("log_w_rows", log_w_rows, (rows, H), T["f32"])])
     st = lib().partition_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_i), _ptr(lse_i),
                                    float(log_w), _ptr(log_w_rows), rows, H, D, _stream(stream))
     _check("partition_lse_merge", st)
@@ -422,10 +496,16 @@ def attn_dense_tara_via(q, k, v, seg, t, seg_host, t_host, strength=2.0, window=
         scale = 1.0 / float(np.sqrt(D))
     if ws is None:
         ws = _workspace(via_workspace_bytes(seg_host, t_host, H, D, dt), q.device)
-    _contig(q, k, v, seg, t, o, lse)
+    T = _dt()
+    if len(seg_host) != n or len(t_host) != n:
+        raise ValueError(f"attn_dense_tara_via: seg_host/t_host need {n} rows")
+    _check_args("attn_dense_tara_via", q, [
+        ("k", k, (n, H, D), (q.dtype,)), ("v", v, (n, H, D), (q.dtype,)),
+        ("seg", seg, (n,), T["u8"]), ("t", t, (n,), T["f32"]),
+        ("o", o, (n, H, D), T["bf16f32"]), ("lse", lse, (n, H), T["f32"])], ws)
     st = lib().attn_dense_tara_via(_ptr(q), _ptr(k), _ptr(v), dt, n, H, D, _ptr(seg), _ptr(t),
                                    _np_ptr(seg_host), _np_ptr(t_host), strength, window,
                                    falloff, cap, scale, _ptr(o), _dtype_code(o), _ptr(lse),
-                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                                   _ptr(ws), _nbytes(ws), _stream(stream))
     _check("attn_dense_tara_via", st)
     return o, lse

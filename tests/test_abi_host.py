@@ -296,3 +296,26 @@ def test_int8_entry_points_reject_bad_arguments():
     bad = list(sp)
     bad[14] = 32        # 32-row blocks
     assert L.attn_block_sparse_int8qk(*bad, None, None, 0, *rest) == -2
+
+
+def test_binding_rejects_host_tensors():
+    """The binding checks each tensor before its pointer reaches the library: host
+    (CPU) tensors are refused without any HIP call."""
+    import torch
+    q = torch.zeros((64, 1, 64), dtype=torch.bfloat16)
+    seg = torch.zeros(64, dtype=torch.uint8)
+    t = torch.zeros(64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="current GPU"):
+        api.attn_dense_tara(q, q, q, seg, t, seg, t)
+    with pytest.raises(ValueError, match="current GPU"):
+        api.attn_block_router(q, q, seg, 0, 1, 0)
+    with pytest.raises(ValueError, match="current GPU"):
+        api.quantize_int8(q)
+
+
+def test_workspace_byte_count():
+    """Workspace sizes are passed in bytes whatever the tensor's dtype."""
+    import torch
+    assert api._nbytes(None) == 0
+    assert api._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
+    assert api._nbytes(torch.zeros((3, 5), dtype=torch.uint8)) == 15

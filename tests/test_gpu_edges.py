@@ -121,3 +121,51 @@ def test_int8_zero_rows():
                               int8_qk=True)
     o_ref, l_ref = _assemble(ref, wl.n, 2, 128, 64)
     compare(o, lse, o_ref, l_ref, "bf16", "int8 zero rows")
+
+
+def test_binding_rejects_mismatched_buffers():
+    """Buffers of the wrong shape, dtype or device are refused by the binding before any
+    launch (they would otherwise be read or written out of range on the GPU)."""
+    n, H, D = 200, 2, 64
+    dev = torch.device("cuda", torch.cuda.current_device())
+    q = torch.zeros((n, H, D), dtype=torch.bfloat16, device=dev)
+    seg = torch.zeros(n, dtype=torch.uint8, device=dev)
+    t = torch.zeros(n, dtype=torch.float32, device=dev)
+    nb = (n + 63) // 64
+    tiles = torch.zeros((H, nb, 2), dtype=torch.int32, device=dev)
+    prot = torch.zeros(1, dtype=torch.int32, device=dev)
+    print("case binding checks", flush=True)
+    bad_dense = [
+        (dict(k=q[:, :1].contiguous()), ValueError),          # heads differ
+        (dict(v=q.float()), TypeError),                        # dtype differs from q
+        (dict(q_seg=t), TypeError),                            # seg must be uint8
+        (dict(k_t=t[:100]), ValueError),                       # too short
+        (dict(o=torch.zeros((n, H, D), dtype=torch.float16, device=dev)), TypeError),
+        (dict(lse=torch.zeros((H, n), dtype=torch.float32, device=dev)), ValueError),
+        (dict(ws=torch.zeros(1 << 20, dtype=torch.uint8)), ValueError),   # host workspace
+        (dict(k=q.transpose(0, 1)), ValueError),               # not contiguous
+    ]
+    for kw, err in bad_dense:
+        args = dict(q=q, k=q, v=q, q_seg=seg, q_t=t, k_seg=seg, k_t=t)
+        args.update(kw)
+        with pytest.raises(err):
+            api.attn_dense_tara(**args)
+    bad_sparse = [
+        (dict(tiles=tiles[:, :nb - 1].contiguous()), ValueError),   # one query block short
+        (dict(tiles=tiles.long()), TypeError),
+        (dict(prot=prot.reshape(1, 1)), ValueError),
+        (dict(seg=seg[:n - 1]), ValueError),
+    ]
+    for kw, err in bad_sparse:
+        args = dict(q=q, k=q, v=q, seg=seg, t=t, tiles=tiles, prot=prot)
+        args.update(kw)
+        with pytest.raises(err):
+            api.attn_block_sparse(**args)
+    with pytest.raises(ValueError):
+        api.attn_block_sparse_tail(q, q, q, seg, t, tiles, prot,
+                                   torch.zeros((H, nb - 1), dtype=torch.float32, device=dev),
+                                   torch.zeros((H, nb, D), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        api.attn_block_router(q, q, seg, 0, 2, 1, tiles=torch.zeros((H, nb, 3), dtype=torch.int32,
+                                                                    device=dev), prot=prot)
+    torch.cuda.synchronize()
