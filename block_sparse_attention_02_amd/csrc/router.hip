@@ -190,7 +190,6 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           TailArgs tail) {
   static_assert(QB == 1 || QB == 4, "query blocks per workgroup");
   extern __shared__ float sc[];  // [QB][nv] pooled scores
-  __shared__ __attribute__((aligned(16))) float qs[D][QB];  // qbar, d-major
   __shared__ int hist[kTopkWaves][256];
   const int h = blockIdx.y;
   const int qb0 = blockIdx.x * QB;
@@ -199,13 +198,14 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const int w = tid >> 6;
   const int nv = counts[1];
 
-  for (int e = tid; e < QB * D; e += 256) {
-    const int j = e / D, d = e % D;
-    qs[d][j] = (qb0 + j < nb) ? qbar[((int64_t)h * nb + qb0 + j) * D + d] : 0.f;
-  }
-  __syncthreads();
+  // The QB query means sit at workgroup-uniform addresses, so they arrive by scalar
+  // loads into SGPRs and the score loop reads nothing from LDS. A query block past the
+  // end reads the last block's means; its scores are never used.
+  const float* qrow[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) qrow[j] = qbar + ((int64_t)h * nb + min(qb0 + j, nb - 1)) * D;
   // Lanes take consecutive video tiles, so each d reads one coalesced run of the
-  // d-major kbar; the QB query means of that d come from one LDS read.
+  // d-major kbar.
   const float* kh = kbar + (int64_t)h * D * nb;
   for (int vi = tid; vi < nv; vi += 256) {
     const int kb = video[vi];
@@ -215,13 +215,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 #pragma unroll 8
     for (int d = 0; d < D; ++d) {
       const float kv = kh[(int64_t)d * nb + kb];
-      if (QB == 4) {
-        const f32x4 q4 = *(const f32x4*)&qs[d][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = acc[j] + mul_rounded(q4[j], kv);
-      } else {
-        acc[0] = acc[0] + mul_rounded(qs[d][0], kv);
-      }
+      for (int j = 0; j < QB; ++j) acc[j] = acc[j] + mul_rounded(qrow[j][d], kv);
     }
 #pragma unroll
     for (int j = 0; j < QB; ++j) sc[j * nv + vi] = acc[j];
