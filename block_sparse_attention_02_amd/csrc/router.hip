@@ -2,7 +2,8 @@
 //
 // "H3 SLA Attention", "How it works": a single product of the block-mean queries with
 // the block-mean keys rates each (query block, key block) pair, and a query block keeps
-// the highest-rated (1 - sparsity) share of the key blocks; inputs table: blocks overlapping language or audio rows are always attended.
+// the highest-rated (1 - sparsity) share of the key blocks; inputs table: blocks
+// overlapping language or audio rows are always attended.
 // "H3 sparse-attention breakpoints": the density is a fraction of the video KV tiles.
 //
 // Three kernels, all deterministic (no floating-point atomics):
@@ -384,17 +385,27 @@ __global__ __launch_bounds__(64 * (D / 32)) void tail_v_kernel(const float* __re
   const int qb0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int kend = (counts[1] + 7) & ~7;  // video tiles, in steps of 8 (<= nbp)
+  // video tiles in steps of 32: nbp is a multiple of 32 and both operands are zero past
+  // the video count, so the extra products are 0 x 0; four steps of loads are in flight
+  const int kend = (counts[1] + 31) & ~31;
   const bool row_ok = qb0 + l32 < nb;
   const float* arow = wts + ((int64_t)h * nb + (row_ok ? qb0 + l32 : 0)) * nbp + 4 * hh;
   const float* brow = vbt + ((int64_t)h * D + 32 * w + l32) * nbp + 4 * hh;
   f32x16 acc = {};
-  for (int k0 = 0; k0 < kend; k0 += 8) {
-    f32x4 a = *(const f32x4*)(arow + k0);
-    if (!row_ok) a = f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 b = *(const f32x4*)(brow + k0);
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    f32x4 a[4], b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *(const f32x4*)(arow + k0 + 8 * u);
+      b[u] = *(const f32x4*)(brow + k0 + 8 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!row_ok) a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][j], b[u][j], acc, 0, 0, 0);
+    }
   }
   // lane holds column 32w + l32 and rows 8(r/4) + 4hh + r%4
 #pragma unroll
