@@ -143,12 +143,14 @@ def test_p1_shape_dense_tara_sampled(micro, path):
     compare(o[ri][:, P1_HEADS], lse[ri][:, P1_HEADS], o_ref, l_ref, "bf16", f"p1 shape {path}")
 
 
-def test_full_sparse_with_tail_sampled(full):
-    """Full scale, s = 0.90, TARA on routed guide tiles plus the pooled tail key: tail
-    terms of the sampled heads against the oracle, outputs on sampled rows."""
+@pytest.mark.parametrize("sparsity", [0.90, 0.95])
+def test_full_sparse_with_tail_sampled(full, sparsity):
+    """Full scale, TARA on routed guide tiles plus the pooled tail key (at s = 0.95 the
+    tail key carries the largest share of a row's weight): tail terms of the sampled heads
+    against the oracle, outputs on sampled rows."""
     wl, seg, t, dev, host, host32 = full
-    plan = api.router_plan(seg, wl.protected_prefix_len, 0.90)
-    print("router + tail 116883 x 56, s=0.90", flush=True)
+    plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
+    print(f"router + tail 116883 x 56, s={sparsity}", flush=True)
     tiles, prot, tl, tv = api.attn_block_router_tail(dev["q"], dev["k"], dev["v"], dev["seg"],
                                                      wl.protected_prefix_len, plan["k_sel"],
                                                      plan["n_prot"], scale=wl.scale)
@@ -177,7 +179,7 @@ def test_full_sparse_with_tail_sampled(full):
         orf.append(ob)
         lrf.append(lb)
     compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
-            "full sparse tail s=0.9")
+            f"full sparse tail s={sparsity}")
 
 
 @pytest.mark.parametrize("bs", [32, 128])
