@@ -72,7 +72,7 @@ def test_full_dense_via_sampled(full):
     compare(o[ri][:, HEADS], lse[ri][:, HEADS], o_ref, l_ref, "bf16", "full dense via")
 
 
-@pytest.mark.parametrize("sparsity", [0.90, 0.50])
+@pytest.mark.parametrize("sparsity", [0.90, 0.50, 0.70, 0.85, 0.95])
 def test_full_router_and_sparse_sampled(full, sparsity):
     wl, seg, t, dev, host, host32 = full
     plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
