@@ -8,11 +8,14 @@ One step = one pass of the whole hot path over the full-scale packed sequence
      guide tiles;
   3. dense TARA through the positive-partition decomposition with LSE merges
      (attn_dense_tara_via).
-Each of the three produces a full attention output, i.e. 4*N^2*d*H = 391.71
-dense-equivalent TFLOP; ``value`` is 3 x 391.71 TFLOP / step time. Per-call
-ms, dense-equivalent TFLOP/s and fraction of the bf16 MFMA peak are reported
-beside it, with a sparsity sweep, the roofline of the dominant kernel (the
-dense TARA attention kernel) and the float64 CPU oracle timed on a sample.
+``value`` is the dense TARA call's dense-equivalent throughput,
+4*N^2*d*H = 391.71 TFLOP over its median ms/call (HIP events on the launch
+stream); ``ms_per_step`` is the wall time of the whole step. The block-sparse
+call is reported as router + sparse ms and its speed-up over the dense call
+(its executed work is a fraction of the dense work, so it is not folded into a
+dense-equivalent rate), the partition path as ms and dense-equivalent TFLOP/s.
+Beside them: a sparsity sweep, the roofline of the dominant kernel (the dense
+TARA attention kernel) and the float64 CPU oracle timed on a sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -166,6 +169,45 @@ def cpu_baseline(wl, q, k, v, seg, t):
                       f"{len(heads)} heads ({flops / 1e12:.3f} dense TFLOP) in {dt:.1f} s"}
 
 
+def call_summaries(rows, dense_flop, sparsity, k_sel, n_prot, kept):
+    """Per-call figures from the HIP-event times (ms) of the timed steps: medians, the
+    dense-equivalent rate of the two full-attention calls, and the block-sparse call as
+    router + sparse ms with its speed-up over the dense call."""
+    def summary(name):
+        xs = rows.get(name) or []
+        if not xs:
+            return None
+        return {"ms": float(np.median(xs)), "ms_mean": float(np.mean(xs)), "n": len(xs)}
+
+    calls = {}
+    d = summary("dense")
+    if d:
+        tf = dense_flop / (d["ms"] * 1e-3) / 1e12
+        calls["dense_tara"] = dict(d, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
+    r, s = summary("router"), summary("sparse")
+    if r and s:
+        tot = r["ms"] + s["ms"]
+        calls["block_sparse"] = {
+            "sparsity": sparsity, "k_sel": k_sel, "n_prot": n_prot, "kept_frac": kept,
+            "router_ms": r["ms"], "sparse_ms": s["ms"], "ms": tot,
+            "executed_tflops": kept * dense_flop / (s["ms"] * 1e-3) / 1e12,
+            "speedup_vs_dense": (d["ms"] / tot) if d else None,
+            "target_speedup": 0.8 / kept,
+        }
+    vi = summary("via")
+    if vi:
+        tf = dense_flop / (vi["ms"] * 1e-3) / 1e12
+        calls["dense_tara_via"] = dict(vi, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
+    return calls
+
+
+def headline_value(calls):
+    """``value``: the dense TARA call's dense-equivalent TFLOP/s (None on a profiling run
+    that leaves the dense call out)."""
+    d = calls.get("dense_tara")
+    return d["dense_equiv_tflops"] if d else None
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -266,37 +308,9 @@ def main():
     print(f"# timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
 
     ms_step = wall * 1e3 / args.steps
-    n_calls = {"all": 3, "dense": 1, "sparse": 1, "via": 1}[args.only]
-    value = n_calls * dense_flop / (ms_step * 1e-3) / 1e12
-
-    def summary(name):
-        xs = rows[name]
-        if not xs:
-            return None
-        med = float(np.median(xs))
-        return {"ms": med, "ms_mean": float(np.mean(xs)), "n": len(xs)}
-
-    calls = {}
-    d = summary("dense")
-    if d:
-        tf = dense_flop / (d["ms"] * 1e-3) / 1e12
-        calls["dense_tara"] = dict(d, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
-    r, s = summary("router"), summary("sparse")
-    if r and s:
-        tot = r["ms"] + s["ms"]
-        tf = dense_flop / (tot * 1e-3) / 1e12
-        calls["block_sparse"] = {
-            "sparsity": args.sparsity, "k_sel": k_sel, "n_prot": n_prot, "kept_frac": kept,
-            "router_ms": r["ms"], "sparse_ms": s["ms"], "ms": tot,
-            "dense_equiv_tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS,
-            "executed_tflops": kept * dense_flop / (s["ms"] * 1e-3) / 1e12,
-            "speedup_vs_dense": (d["ms"] / tot) if d else None,
-            "target_speedup": 0.8 / kept,
-        }
-    vi = summary("via")
-    if vi:
-        tf = dense_flop / (vi["ms"] * 1e-3) / 1e12
-        calls["dense_tara_via"] = dict(vi, dense_equiv_tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS)
+    calls = call_summaries(rows, dense_flop, args.sparsity, k_sel, n_prot, kept)
+    value = headline_value(calls)
+    d = calls.get("dense_tara")
 
     sweep = {}
     if not args.no_sweep and args.only in ("all", "sparse"):
@@ -492,8 +506,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "packed sequence 116,883 rows x 56 heads x d 128 bf16: dense "
-                               "TARA direct + router/block-sparse s=%.2f + partition path"
-                               % args.sparsity,
+                               "TARA direct + router/block-sparse s=%.2f + partition path; "
+                               "value = the dense TARA call" % args.sparsity,
                    "rows": N, "heads": H, "head_dim": D, "block_size": 64,
                    "sparsity": args.sparsity, "step_rows": args.only,
                    "tara": {"strength": tara[0], "window": tara[1], "falloff": tara[2],

@@ -50,3 +50,33 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, tag=""):
     assert rel <= tol["rel_l2"], (tag, rel)
     assert lerr <= tol["lse"], (tag, lerr)
     return err, rel, lerr
+
+
+def oracle_routes(wl, q, k, seg, k_sel, heads, bs=64):
+    """The oracle's routing for the given heads of seeded inputs q, k [n, H, d]:
+    (tiles [len(heads), nb, k_sel] with -1 past the video-tile count, as the
+    library writes them; protected block indices)."""
+    import oracle
+    nb, prot, video, _ = oracle.router_plan(seg, wl.protected_prefix_len, bs, 0.0)
+    kk = min(k_sel, len(video))
+    tiles = np.full((len(heads), nb, k_sel), -1, dtype=np.int64)
+    for j, h in enumerate(heads):
+        tiles[j, :, :kk] = oracle.route_head(W.to_float32(q[:, h], wl.dtype),
+                                             W.to_float32(k[:, h], wl.dtype), seg,
+                                             wl.protected_prefix_len, bs, kk)
+    return tiles, prot
+
+
+def checked_routes(tiles_gpu, prot_gpu, wl, q, k, seg, k_sel, heads, bs=64, tag=""):
+    """Asserts that the GPU router's tile lists (rows ``heads`` of ``tiles_gpu``) and
+    protected list equal the oracle's bit for bit, then returns the oracle's own lists
+    (tiles for ``heads``, prot), so that no oracle input comes from the GPU."""
+    tiles_ref, prot_ref = oracle_routes(wl, q, k, seg, k_sel, heads, bs)
+    got_p = (prot_gpu.cpu().numpy() if prot_gpu is not None and prot_gpu.numel()
+             else np.zeros(0, dtype=np.int64))
+    assert np.array_equal(got_p, prot_ref), f"{tag}: protected list differs from the oracle"
+    if k_sel > 0:
+        got = tiles_gpu.cpu().numpy()[list(heads)]
+        mism = int(np.sum(np.any(got != tiles_ref, axis=2)))
+        assert mism == 0, f"{tag}: {mism} tile lists differ from the oracle"
+    return tiles_ref, prot_ref

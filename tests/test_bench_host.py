@@ -65,3 +65,22 @@ def test_code_hash_ignores_comments_and_blank_lines():
     b = "int x = 1;\nint y = 2;  // two\n"
     c = "int x = 1;\nint y = 3;\n"
     assert bench.code_hash(a) == bench.code_hash(b) != bench.code_hash(c)
+
+
+def test_value_is_the_dense_call():
+    """The headline value is the dense TARA call's dense-equivalent TFLOP/s (median
+    ms/call); the block-sparse call carries ms and its speed-up, no dense-equivalent
+    rate."""
+    flop = 391.71e12
+    rows = {"dense": [330.0, 320.0, 325.0], "router": [3.0, 2.8, 2.9],
+            "sparse": [66.0, 65.0, 67.0], "via": [350.0, 351.0, 352.0]}
+    calls = bench.call_summaries(rows, flop, 0.9, 170, 130, 300 / 1827)
+    value = bench.headline_value(calls)
+    assert value == calls["dense_tara"]["dense_equiv_tflops"]
+    assert value == pytest.approx(flop / 0.325 / 1e12)
+    sp = calls["block_sparse"]
+    assert "dense_equiv_tflops" not in sp and "frac_peak" not in sp
+    assert sp["ms"] == pytest.approx(2.9 + 66.0)
+    assert sp["speedup_vs_dense"] == pytest.approx(325.0 / 68.9)
+    assert bench.headline_value(bench.call_summaries({"sparse": [1.0], "router": [1.0]}, flop,
+                                                     0.9, 170, 130, 0.16)) is None

@@ -7,8 +7,8 @@ import torch
 
 import oracle
 from block_sparse_attention_02_amd import api, workloads as W
-from gpu_common import compare, f64, layout_device, to_device
-from test_gpu_small import _route_oracle, _tails_oracle
+from gpu_common import checked_routes, compare, f64, layout_device, to_device
+from test_gpu_small import _tails_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -43,15 +43,12 @@ def _run(wl, prefix, sparsity, bs, dtype, tail=False, n_prot_override=None):
                                        *wl.tara, scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
     heads = wl.heads
-    nb = plan["nb"]
-    tl_np = (tiles.cpu().numpy() if tiles is not None
-             else np.zeros((heads, nb, 0), dtype=np.int32))
-    if plan["k_sel"]:
-        assert np.array_equal(tl_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(heads), bs=bs))
-    tails = _tails_oracle(wl, q, k, v, seg, tl_np, range(heads), bs=bs) if tail else None
-    pr = prot.cpu().numpy() if plan["n_prot"] else np.zeros(0, dtype=np.int32)
+    # the oracle's own lists, after checking that the GPU router wrote the same
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(heads), bs=bs,
+                                tag=f"{wl.name} bs={bs}")
+    tails = _tails_oracle(wl, q, k, v, seg, tl_ref, range(heads), bs=bs) if tail else None
     ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
-                              wl.scale, bs, pr, tl_np, tails=tails)
+                              wl.scale, bs, pr, tl_ref, tails=tails)
     o_ref, l_ref = _assemble(ref, wl.n, heads, wl.head_dim, bs)
     compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} bs={bs} {dtype} tail={tail}")
     return tails
@@ -116,9 +113,10 @@ def test_int8_zero_rows():
     o, lse = api.attn_block_sparse_int8qk(qd, kd, vd, seg_d, t_d, tiles, prot, None, None, 0,
                                           *wl.tara, scale=wl.scale)
     torch.cuda.synchronize()
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(2),
+                                tag="int8 zero rows")
     ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
-                              wl.scale, 64, prot.cpu().numpy(), tiles.cpu().numpy(),
-                              int8_qk=True)
+                              wl.scale, 64, pr, tl_ref, int8_qk=True)
     o_ref, l_ref = _assemble(ref, wl.n, 2, 128, 64)
     compare(o, lse, o_ref, l_ref, "bf16", "int8 zero rows")
 

@@ -1,9 +1,13 @@
 """GPU parity at the full 116,883-row x 56-head size, in the same launch
-configuration the benchmark times, on sampled outputs the oracle computes one
-by one: 3 heads x 8 fixed query blocks (segment boundaries and the 19-row tail)
-plus 4 seeded random blocks. Router tile lists are compared bit-exactly for the
-sampled heads in full."""
+configuration the benchmark times.
+- Router: every tile list of all 56 heads bit-exact against the oracle, at each
+  sparsity of the sweep (block 64) and at blocks of 32 and 128 (s = 0.90).
+- Outputs: sampled rows the oracle computes one by one, 3 heads x 8 fixed query
+  blocks (segment boundaries and the 19-row tail) plus 16 seeded random blocks.
+  The oracle attends with its own tile lists, after the GPU lists were checked
+  equal to them."""
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -11,17 +15,46 @@ import torch
 
 import oracle
 from block_sparse_attention_02_amd import api, workloads as W
-from gpu_common import compare, f64, to_device
+from gpu_common import checked_routes, compare, f64, to_device
 
 pytestmark = pytest.mark.gpu
 
 HEADS = [0, 27, 55]
 FIXED_BLOCKS = [0, 113, 500, 962, 970, 977, 1400, 1826]
+ORACLE_THREADS = 16
 
 
 def _blocks():
     rng = np.random.default_rng(2024)
-    return sorted(set(FIXED_BLOCKS) | set(rng.integers(0, 1827, 4).tolist()))
+    extra = [b for b in rng.permutation(1827).tolist() if b not in FIXED_BLOCKS][:16]
+    return sorted(FIXED_BLOCKS + extra)
+
+
+def _oracle_lists(q32, k32, seg, prefix, bs, ks):
+    """The oracle's routing of one head for several routed counts: route_head's steps
+    (block means, pooled scores over the video tiles, top-k), with the pooled scores
+    formed once for all counts in ``ks``. Returns {k: [nb, k] tile lists}."""
+    _, _, video, _ = oracle.router_plan(seg, prefix, bs, 0.0)
+    qbar = oracle.block_means_fp32(q32, bs)
+    kbar = oracle.block_means_fp32(k32, bs)
+    scores = oracle.pooled_scores_fp32(qbar, kbar[video])
+    return {kk: oracle.select_topk(scores, video, kk) for kk in ks}
+
+
+def _all_heads_mismatches(q, k, seg, prefix, bs, got):
+    """Mismatching (head, query block) tile lists of every head: ``got`` maps each routed
+    count k to the GPU lists [H, nb, k]. Heads run in a thread pool (numpy releases the
+    GIL inside its array operations)."""
+    H = q.shape[1]
+
+    def one(h):
+        ref = _oracle_lists(W.to_float32(q[:, h], "bf16"), W.to_float32(k[:, h], "bf16"), seg,
+                            prefix, bs, list(got))
+        return {kk: int(np.sum(np.any(got[kk][h] != ref[kk], axis=1))) for kk in got}
+
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        per_head = list(ex.map(one, range(H)))
+    return {kk: sum(m[kk] for m in per_head) for kk in got}
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +68,7 @@ def full():
                seg=torch.from_numpy(seg).cuda(), t=torch.from_numpy(t).cuda())
     host = {n: f64(x[:, HEADS], "bf16") for n, x in (("q", q), ("k", k), ("v", v))}
     host32 = {n: W.to_float32(x[:, HEADS], "bf16") for n, x in (("q", q), ("k", k))}
-    return wl, seg, t, dev, host, host32
+    return wl, seg, t, dev, host, host32, (q, k, v)
 
 
 def _sample_rows(blocks, n):
@@ -49,7 +82,7 @@ def _dense_ref(wl, seg, t, host, rows):
 
 
 def test_full_dense_direct_sampled(full):
-    wl, seg, t, dev, host, _ = full
+    wl, seg, t, dev, host, _, _ = full
     print("dense direct 116883 x 56", flush=True)
     o, lse = api.attn_dense_tara(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], dev["seg"],
                                  dev["t"], *wl.tara, scale=wl.scale)
@@ -61,7 +94,7 @@ def test_full_dense_direct_sampled(full):
 
 
 def test_full_dense_via_sampled(full):
-    wl, seg, t, dev, host, _ = full
+    wl, seg, t, dev, host, _, _ = full
     print("dense via partitions 116883 x 56", flush=True)
     o, lse = api.attn_dense_tara_via(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], seg, t,
                                      *wl.tara, scale=wl.scale)
@@ -74,7 +107,7 @@ def test_full_dense_via_sampled(full):
 
 @pytest.mark.parametrize("sparsity", [0.90, 0.50, 0.70, 0.85, 0.95])
 def test_full_router_and_sparse_sampled(full, sparsity):
-    wl, seg, t, dev, host, host32 = full
+    wl, seg, t, dev, host, host32, raw = full
     plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
     assert plan["n_prot"] == 130 and plan["n_video"] == 1697
     print(f"router + sparse s={sparsity} k={plan['k_sel']}", flush=True)
@@ -83,16 +116,8 @@ def test_full_router_and_sparse_sampled(full, sparsity):
     o, lse = api.attn_block_sparse(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], tiles,
                                    prot, *wl.tara, scale=wl.scale)
     torch.cuda.synchronize()
-    tl = tiles.cpu().numpy()[HEADS]
-    pr = prot.cpu().numpy()
-    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, 64, sparsity)
-    assert np.array_equal(pr, prot_ref)
-    for j in range(len(HEADS)):
-        ref = oracle.route_head(host32["q"][:, j], host32["k"][:, j], seg,
-                                wl.protected_prefix_len, 64, plan["k_sel"])
-        mism = int(np.sum(np.any(tl[j] != ref, axis=1)))
-        print(f"head {HEADS[j]}: {mism} mismatching tile lists of 1827", flush=True)
-        assert mism == 0
+    tl, pr = checked_routes(tiles, prot, wl, raw[0], raw[1], seg, plan["k_sel"], HEADS,
+                            tag=f"full s={sparsity}")
     blocks = _blocks()
     ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64, pr,
                               tl, heads=range(len(HEADS)), qblocks=blocks)
@@ -105,6 +130,51 @@ def test_full_router_and_sparse_sampled(full, sparsity):
         lrf.append(lb)
     compare(torch.cat(og), torch.cat(lg), np.concatenate(orf), np.concatenate(lrf), "bf16",
             f"full sparse s={sparsity}")
+
+
+def test_full_router_all_heads_bit_exact(full):
+    """Every tile list of all 56 heads x 1,827 query blocks against the oracle at each
+    sparsity of the sweep (block 64), and the protected list."""
+    wl, seg, t, dev, host, host32, raw = full
+    got = {}
+    for sparsity in wl.sparsities:
+        plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
+        tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"],
+                                            wl.protected_prefix_len, plan["k_sel"],
+                                            plan["n_prot"])
+        torch.cuda.synchronize()
+        _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, 64, sparsity)
+        assert np.array_equal(prot.cpu().numpy(), prot_ref)
+        got[plan["k_sel"]] = tiles.cpu().numpy()
+    print(f"router all heads, k = {sorted(got)}", flush=True)
+    # the shared-scores helper is route_head's composition: check it on one head and count
+    q32, k32 = W.to_float32(raw[0][:, 55], "bf16"), W.to_float32(raw[1][:, 55], "bf16")
+    assert np.array_equal(_oracle_lists(q32, k32, seg, wl.protected_prefix_len, 64, [170])[170],
+                          oracle.route_head(q32, k32, seg, wl.protected_prefix_len, 64, 170))
+    t0 = time.time()
+    mism = _all_heads_mismatches(raw[0], raw[1], seg, wl.protected_prefix_len, 64, got)
+    print(f"oracle lists of 56 heads in {time.time() - t0:.1f}s; mismatching lists per k: "
+          f"{mism}", flush=True)
+    assert all(m == 0 for m in mism.values())
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_full_router_all_heads_block_sizes(full, bs):
+    """Every tile list of all 56 heads at blocks of 32 and 128 rows, s = 0.90."""
+    wl, seg, t, dev, host, host32, raw = full
+    plan = api.router_plan(seg, wl.protected_prefix_len, 0.90, block_size=bs)
+    tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
+                                        plan["k_sel"], plan["n_prot"], block_size=bs)
+    torch.cuda.synchronize()
+    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, bs, 0.90)
+    assert np.array_equal(prot.cpu().numpy(), prot_ref)
+    print(f"router all heads bs={bs} k={plan['k_sel']}", flush=True)
+    t0 = time.time()
+    mism = _all_heads_mismatches(raw[0], raw[1], seg, wl.protected_prefix_len, bs,
+                                 {plan["k_sel"]: tiles.cpu().numpy()})
+    print(f"oracle lists of 56 heads (bs={bs}) in {time.time() - t0:.1f}s; mismatching "
+          f"lists: {mism}", flush=True)
+    assert all(m == 0 for m in mism.values())
 
 
 # ------------------------------------------------------------------ isolated shape
@@ -148,7 +218,7 @@ def test_full_sparse_with_tail_sampled(full, sparsity):
     """Full scale, TARA on routed guide tiles plus the pooled tail key (at s = 0.95 the
     tail key carries the largest share of a row's weight): tail terms of the sampled heads
     against the oracle, outputs on sampled rows."""
-    wl, seg, t, dev, host, host32 = full
+    wl, seg, t, dev, host, host32, raw = full
     plan = api.router_plan(seg, wl.protected_prefix_len, sparsity)
     print(f"router + tail 116883 x 56, s={sparsity}", flush=True)
     tiles, prot, tl, tv = api.attn_block_router_tail(dev["q"], dev["k"], dev["v"], dev["seg"],
@@ -157,11 +227,12 @@ def test_full_sparse_with_tail_sampled(full, sparsity):
     o, lse = api.attn_block_sparse_tail(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"], tiles,
                                         prot, tl, tv, *wl.tara, scale=wl.scale)
     torch.cuda.synchronize()
-    tl_np = tiles.cpu().numpy()
+    tl_ref, pr = checked_routes(tiles, prot, wl, raw[0], raw[1], seg, plan["k_sel"], HEADS,
+                                tag=f"full tail s={sparsity}")
     tails = {}
     for j, h in enumerate(HEADS):
         tails[j] = oracle.tail_terms(host32["q"][:, j], host32["k"][:, j], host["v"][:, j], seg,
-                                     wl.protected_prefix_len, 64, tl_np[h], wl.scale)
+                                     wl.protected_prefix_len, 64, tl_ref[j], wl.scale)
         fin = np.isfinite(tails[j][0])
         el = float(np.max(np.abs(tl[h].cpu().numpy()[fin] - tails[j][0][fin])))
         ev = float(np.max(np.abs(tv[h].cpu().numpy() - tails[j][1])))
@@ -169,8 +240,7 @@ def test_full_sparse_with_tail_sampled(full, sparsity):
         assert el < 1e-3 and ev < 1e-3
     blocks = _blocks()
     ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64,
-                              prot.cpu().numpy(), tl_np[HEADS], heads=range(3), qblocks=blocks,
-                              tails=tails)
+                              pr, tl_ref, heads=range(3), qblocks=blocks, tails=tails)
     og, lg, orf, lrf = [], [], [], []
     for (j, qb), (ob, lb) in ref.items():
         lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
@@ -188,7 +258,7 @@ def test_full_block_sizes_with_audio_sinks_sampled(full, bs):
     sink query blocks dense: router lists of the sampled heads bit-exact, outputs of
     sampled blocks (segment boundaries, the audio span, the ragged tail) against the
     oracle."""
-    wl, seg, t, dev, host, host32 = full
+    wl, seg, t, dev, host, host32, raw = full
     plan = api.router_plan(seg, wl.protected_prefix_len, 0.90, block_size=bs)
     print(f"router + sparse + audio sinks bs={bs} k={plan['k_sel']}", flush=True)
     tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
@@ -197,17 +267,8 @@ def test_full_block_sizes_with_audio_sinks_sampled(full, bs):
                                          tiles, prot, 1 << W.SEG_AUDIO, None, None, *wl.tara,
                                          scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
-    tl = tiles.cpu().numpy()[HEADS]
-    pr = prot.cpu().numpy()
-    _, prot_ref, _, _ = oracle.router_plan(seg, wl.protected_prefix_len, bs, 0.90)
-    assert np.array_equal(pr, prot_ref)
-    for j in range(len(HEADS)):
-        ref = oracle.route_head(host32["q"][:, j], host32["k"][:, j], seg,
-                                wl.protected_prefix_len, bs, plan["k_sel"])
-        mism = int(np.sum(np.any(tl[j] != ref, axis=1)))
-        print(f"bs={bs} head {HEADS[j]}: {mism} mismatching tile lists of {plan['nb']}",
-              flush=True)
-        assert mism == 0
+    tl, pr = checked_routes(tiles, prot, wl, raw[0], raw[1], seg, plan["k_sel"], HEADS, bs=bs,
+                            tag=f"full bs={bs}")
     nb = plan["nb"]
     # blocks holding rows 0, 7258/7259 (text/guide), 61570/61571 (guide/audio), 62000
     # (audio), 62570/62571 (audio/output), 90000 and the last row
@@ -231,7 +292,7 @@ def test_full_block_sizes_with_audio_sinks_sampled(full, bs):
 def test_full_sparse_int8qk_sampled(full):
     """Full scale, s = 0.90, block 64, TARA on routed guide tiles, int8 QK product:
     sampled rows against the oracle's attention on the dequantized q and k."""
-    wl, seg, t, dev, host, host32 = full
+    wl, seg, t, dev, host, host32, raw = full
     plan = api.router_plan(seg, wl.protected_prefix_len, 0.90)
     print("router + int8 QK sparse 116883 x 56, s=0.90", flush=True)
     tiles, prot = api.attn_block_router(dev["q"], dev["k"], dev["seg"], wl.protected_prefix_len,
@@ -239,11 +300,11 @@ def test_full_sparse_int8qk_sampled(full):
     o, lse = api.attn_block_sparse_int8qk(dev["q"], dev["k"], dev["v"], dev["seg"], dev["t"],
                                           tiles, prot, None, None, 0, *wl.tara, scale=wl.scale)
     torch.cuda.synchronize()
-    tl = tiles.cpu().numpy()[HEADS]
+    tl, pr = checked_routes(tiles, prot, wl, raw[0], raw[1], seg, plan["k_sel"], HEADS,
+                            tag="full int8")
     blocks = _blocks()
     ref = oracle.block_sparse(host["q"], host["k"], host["v"], seg, t, wl.tara, wl.scale, 64,
-                              prot.cpu().numpy(), tl, heads=range(len(HEADS)), qblocks=blocks,
-                              int8_qk=True)
+                              pr, tl, heads=range(len(HEADS)), qblocks=blocks, int8_qk=True)
     og, lg, orf, lrf = [], [], [], []
     for (j, qb), (ob, lb) in ref.items():
         lo, hi = qb * 64, min(wl.n, qb * 64 + 64)

@@ -8,8 +8,8 @@ import torch
 
 import oracle
 from block_sparse_attention_02_amd import api, workloads as W
-from gpu_common import compare, f64, layout_device, to_device
-from test_gpu_small import _route_oracle, _tails_oracle
+from gpu_common import checked_routes, compare, f64, layout_device, to_device
+from test_gpu_small import _tails_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -88,10 +88,11 @@ def test_sparse_int8qk_small(bs, sparsity, tail, sinks, d):
     o16, l16 = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, mask, tl, tv,
                                            *wl.tara, scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
-    tiles_np = tiles.cpu().numpy()
-    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3), bs=bs) if tail else None
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(3), bs=bs,
+                                tag=f"int8 bs={bs} s={sparsity}")
+    tails = _tails_oracle(wl, q, k, v, seg, tl_ref, range(3), bs=bs) if tail else None
     ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
-                              wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails,
+                              wl.scale, bs, pr, tl_ref, tails=tails,
                               sink_segments=(W.SEG_AUDIO,) if sinks else (), int8_qk=True)
     o_ref, l_ref = _assemble(ref, wl.n, 3, d, bs)
     compare(o, lse, o_ref, l_ref, "bf16",

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from block_sparse_attention_02_amd import api, workloads as W
-from gpu_common import compare, f64, layout_device, to_device
+from gpu_common import checked_routes, compare, f64, layout_device, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -190,16 +190,13 @@ def test_sparse_mid_sampled_blocks():
     o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
                                    scale=wl.scale)
     torch.cuda.synchronize()
-    tl = tiles.cpu().numpy()
-    pr = prot.cpu().numpy()
     heads = [0, 11, 23]
-    ref_tiles = _route_oracle(wl, q, k, seg, plan["k_sel"], heads)
-    assert np.array_equal(tl[heads], ref_tiles)
+    tl, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], heads, tag="sparse mid")
     rng = np.random.default_rng(3)
     blocks = sorted(set([0, 1, 14, 15, 200, 253, 254, 492]) | set(rng.integers(0, 493, 12).tolist()))
     q64, k64, v64 = (f64(x[:, heads], "bf16") for x in (q, k, v))
     ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, 64, pr,
-                              tl[heads], heads=range(3), qblocks=blocks)
+                              tl, heads=range(3), qblocks=blocks)
     og, lg, orf, lrf = [], [], [], []
     for (j, qb), (ob, lb) in ref.items():
         lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
@@ -243,10 +240,10 @@ def test_sparse_with_penalty_small(sparsity):
     o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
                                    scale=wl.scale)
     torch.cuda.synchronize()
-    tl = tiles.cpu().numpy()
-    assert np.array_equal(tl, _route_oracle(wl, q, k, seg, plan["k_sel"], range(4)))
+    tl, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(4),
+                            tag=f"sparse pen s={sparsity}")
     ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
-                              wl.scale, 64, prot.cpu().numpy(), tl)
+                              wl.scale, 64, pr, tl)
     o_ref = np.zeros((wl.n, 4, 128))
     l_ref = np.zeros((wl.n, 4))
     for (h, qb), (ob, lb) in ref.items():
@@ -289,13 +286,14 @@ def test_sparse_hand_built_lists(d, dtype):
 
 # ------------------------------------------------------------------- tail term
 
-def _tails_oracle(wl, q, k, v, seg, tiles, heads, bs=64):
-    """oracle.tail_terms for the given heads: {j: (lse [nqb], v [nqb, d])}."""
+def _tails_oracle(wl, q, k, v, seg, tiles_ref, heads, bs=64):
+    """oracle.tail_terms for the given heads: {j: (lse [nqb], v [nqb, d])}; tiles_ref[j]
+    holds the oracle's tile lists of head heads[j]."""
     out = {}
     for j, h in enumerate(heads):
         out[j] = oracle.tail_terms(W.to_float32(q[:, h], wl.dtype), W.to_float32(k[:, h], wl.dtype),
                                    f64(v[:, h], wl.dtype), seg, wl.protected_prefix_len, bs,
-                                   tiles[h], wl.scale)
+                                   tiles_ref[j], wl.scale)
     return out
 
 
@@ -314,7 +312,8 @@ def test_router_tail_terms_mid():
     torch.cuda.synchronize()
     assert torch.equal(tiles, tiles0)
     heads = [0, 11, 23]
-    ref = _tails_oracle(wl, q, k, v, seg, tiles.cpu().numpy(), heads)
+    tl_ref, _ = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], heads, tag="tail mid")
+    ref = _tails_oracle(wl, q, k, v, seg, tl_ref, heads)
     tl, tv = tl.cpu().numpy(), tv.cpu().numpy()
     for j, h in enumerate(heads):
         l_ref, v_ref = ref[j]
@@ -345,10 +344,11 @@ def test_sparse_with_tail_small(dtype, sparsity):
     o, lse = api.attn_block_sparse_tail(qd, kd, vd, seg_d, t_d, tiles, prot, tl, tv, *wl.tara,
                                         scale=wl.scale)
     torch.cuda.synchronize()
-    tiles_np = tiles.cpu().numpy()
-    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3))
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(3),
+                                tag=f"tail {dtype} s={sparsity}")
+    tails = _tails_oracle(wl, q, k, v, seg, tl_ref, range(3))
     ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
-                              wl.scale, 64, prot.cpu().numpy(), tiles_np, tails=tails)
+                              wl.scale, 64, pr, tl_ref, tails=tails)
     o_ref = np.zeros((wl.n, 3, d))
     l_ref = np.zeros((wl.n, 3))
     for (h, qb), (ob, lb) in ref.items():

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from block_sparse_attention_02_amd import api, workloads as W
-from gpu_common import compare, f64, layout_device, to_device
+from gpu_common import checked_routes, compare, f64, layout_device, to_device
 from test_gpu_small import _route_oracle, _tails_oracle
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +73,9 @@ def test_router_tail_terms_block_sizes(bs):
                                                      scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
     heads = [0, 23]
-    ref = _tails_oracle(wl, q, k, v, seg, tiles.cpu().numpy(), heads, bs=bs)
+    tl_ref, _ = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], heads, bs=bs,
+                               tag=f"tail terms bs={bs}")
+    ref = _tails_oracle(wl, q, k, v, seg, tl_ref, heads, bs=bs)
     tl, tv = tl.cpu().numpy(), tv.cpu().numpy()
     for j, h in enumerate(heads):
         l_ref, v_ref = ref[j]
@@ -111,11 +113,11 @@ def test_sparse_block_sizes_small(bs, dtype, sparsity, tail):
         o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles, prot, *wl.tara,
                                        scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
-    tiles_np = tiles.cpu().numpy()
-    assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(3), bs=bs))
-    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3), bs=bs) if tail else None
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(3), bs=bs,
+                                tag=f"sparse bs={bs} {dtype} s={sparsity}")
+    tails = _tails_oracle(wl, q, k, v, seg, tl_ref, range(3), bs=bs) if tail else None
     ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
-                              wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails)
+                              wl.scale, bs, pr, tl_ref, tails=tails)
     o_ref, l_ref = _assemble(ref, wl.n, 3, wl.head_dim, bs)
     compare(o, lse, o_ref, l_ref, dtype, f"sparse bs={bs} {dtype} s={sparsity} tail={tail}")
 
@@ -171,10 +173,11 @@ def test_sparse_audio_sink_blocks(bs, dtype, tail):
     o, lse = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, AUDIO_SINK, tl, tv,
                                          *wl.tara, scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
-    tiles_np = tiles.cpu().numpy()
-    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(3), bs=bs) if tail else None
+    tl_ref, pr = checked_routes(tiles, prot, wl, q, k, seg, plan["k_sel"], range(3), bs=bs,
+                                tag=f"sinks bs={bs} {dtype}")
+    tails = _tails_oracle(wl, q, k, v, seg, tl_ref, range(3), bs=bs) if tail else None
     ref = oracle.block_sparse(f64(q, dtype), f64(k, dtype), f64(v, dtype), seg, t, wl.tara,
-                              wl.scale, bs, prot.cpu().numpy(), tiles_np, tails=tails,
+                              wl.scale, bs, pr, tl_ref, tails=tails,
                               sink_segments=(W.SEG_AUDIO,))
     o_ref, l_ref = _assemble(ref, wl.n, 3, wl.head_dim, bs)
     compare(o, lse, o_ref, l_ref, dtype, f"sinks bs={bs} {dtype} tail={tail}")

@@ -385,6 +385,85 @@ def test_sparsity_zero_routes_every_video_tile():
     assert kk == len(vid) and all(np.array_equal(r, vid) for r in tiles)
 
 
+def _brute_route(q32, k32, seg, prefix, bs, k):
+    """Routing of one head written out with scalar float32 loops ("H3 SLA Attention",
+    "How it works"): block means row by row, the pooled score of query block qb against
+    each video tile kb (qbar[qb] . kbar[kb], products and sums rounded to float32 in d
+    order), and tile kb chosen iff fewer than k video tiles rank above it."""
+    n, d = q32.shape
+    nb = (n + bs - 1) // bs
+
+    def mean(x, b):
+        rows = range(b * bs, min(n, b * bs + bs))
+        out = []
+        for c in range(d):
+            acc = np.float32(0.0)
+            for r in rows:
+                acc = np.float32(acc + x[r, c])
+            out.append(np.float32(acc / np.float32(len(rows))))
+        return out
+
+    video = [b for b in range(nb)
+             if not (b * bs < prefix or any(int(seg[r]) in (W.SEG_TEXT, W.SEG_AUDIO)
+                                            for r in range(b * bs, min(n, b * bs + bs))))]
+    qbar = [mean(q32, b) for b in range(nb)]
+    kbar = {b: mean(k32, b) for b in video}
+    lists = []
+    for qb in range(nb):
+        score = {}
+        for kb in video:
+            acc = np.float32(0.0)
+            for c in range(d):
+                acc = np.float32(acc + np.float32(qbar[qb][c] * kbar[kb][c]))
+            score[kb] = float(acc)
+        chosen = [kb for kb in video
+                  if sum(1 for j in video if score[j] > score[kb]
+                         or (score[j] == score[kb] and j < kb)) < k]
+        lists.append(sorted(chosen))
+    return np.array(lists, dtype=np.int64).reshape(nb, k)
+
+
+def _route_case(seed=17):
+    """A tiny packed sequence with blocks of 4 rows: a text prefix, a guide span, a block
+    mixing guide and audio rows, an output span and a ragged last block; q and k drawn
+    independently, so the score matrix is not symmetric."""
+    rng = np.random.default_rng(seed)
+    seg = np.array([0] * 6 + [1] * 16 + [1, 1, 2, 2] + [3] * 13, dtype=np.uint8)
+    q32 = rng.standard_normal((len(seg), 6)).astype(np.float32)
+    k32 = rng.standard_normal((len(seg), 6)).astype(np.float32)
+    k32[:8] += 3.0   # protected key blocks score highest: they must still never be routed
+    return seg, q32, k32
+
+
+def test_route_head_brute_force_tiny():
+    """route_head equals the scalar brute force for every routed count, with prefixes
+    that cover one, two or no blocks."""
+    seg, q32, k32 = _route_case()
+    for prefix in (0, 6, 8):
+        nb, prot, video, _ = oracle.router_plan(seg, prefix, 4, 0.0)
+        for k in range(0, len(video) + 1):
+            got = oracle.route_head(q32, k32, seg, prefix, 4, k)
+            assert np.array_equal(got, _brute_route(q32, k32, seg, prefix, 4, k)), (prefix, k)
+            assert set(got.ravel().tolist()).isdisjoint(set(prot.tolist()))
+
+
+def test_route_head_pin_catches_planted_mistakes():
+    """Transposed orientation (the key-block mean of the query block against the query
+    means of the tiles) and ranking every key block instead of the video tiles only both
+    fail the brute-force pin."""
+    seg, q32, k32 = _route_case()
+    prefix, k = 6, 3
+    nb, prot, video, _ = oracle.router_plan(seg, prefix, 4, 0.0)
+    want = _brute_route(q32, k32, seg, prefix, 4, k)
+    assert np.array_equal(oracle.route_head(q32, k32, seg, prefix, 4, k), want)
+    qbar = oracle.block_means_fp32(q32, 4)
+    kbar = oracle.block_means_fp32(k32, 4)
+    transposed = oracle.select_topk(oracle.pooled_scores_fp32(kbar, qbar[video]), video, k)
+    assert not np.array_equal(transposed, want)
+    every_block = oracle.select_topk(oracle.pooled_scores_fp32(qbar, kbar), np.arange(nb), k)
+    assert not np.array_equal(every_block, want)
+
+
 # -------------------------------------------------------------- sparse pins
 
 def _sparse_case(seed=300, strength=2.0):
