@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libh3attn.so")
 
 H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE, H3_ENOMEM = 0, -1, -2, -3, -4, -5
+H3_EFORCED = -6
 H3_DTYPE_F32, H3_DTYPE_BF16 = 0, 1
 
 EXPORTS = (
@@ -71,6 +72,7 @@ _lib = None
 
 class H3Error(RuntimeError):
     def __init__(self, func, status):
+        self.func = func
         self.status = status
         super().__init__(f"{func} failed with status {status} ({status_string(status)})")
 

@@ -5,6 +5,8 @@
 // device. Kernels run on the caller's stream; nothing here synchronises.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "../../include/h3attn.h"
@@ -38,6 +40,23 @@ bool blocks_ok(int n, int bs) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Failure injection for the callers' dense fallback: H3ATTN_FORCE_FAIL holds a comma-
+// separated list of call families ("dense", "router", "sparse"). Their entry points then
+// return H3_EFORCED after the argument checks and before any HIP call. Read on every
+// call, so a caller can switch it on and off at run time.
+bool force_fail(const char* family) {
+  const char* e = std::getenv("H3ATTN_FORCE_FAIL");
+  if (!e) return false;
+  const size_t n = std::strlen(family);
+  for (const char* p = e;;) {
+    const char* c = std::strchr(p, ',');
+    const size_t len = c ? (size_t)(c - p) : std::strlen(p);
+    if (len == n && std::strncmp(p, family, n) == 0) return true;
+    if (!c) return false;
+    p = c + 1;
+  }
+}
 
 size_t vt_bytes(int nk, int heads, int head_dim) {
   return (size_t)pad_keys(nk) * (size_t)heads * (size_t)head_dim * sizeof(uint16_t);
@@ -220,6 +239,7 @@ const char* h3attn_status_string(int status) {
     case H3_ELAUNCH: return "kernel launch failed";
     case H3_EWORKSPACE: return "workspace missing or too small";
     case H3_ENOMEM: return "host memory for the call plan could not be allocated";
+    case H3_EFORCED: return "failure forced by H3ATTN_FORCE_FAIL";
     default: return "unknown status";
   }
 }
@@ -242,6 +262,7 @@ int attn_dense_tara(const void* q, const void* k, const void* v, int dtype, int 
   if (dtype == H3_DTYPE_BF16 && nk > kMaxBf16Keys) return H3_EUNSUPPORTED;
   const size_t need = attn_dense_tara_workspace(nk, heads, head_dim, dtype);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
+  if (force_fail("dense")) return H3_EFORCED;
   AttnArgs a = make_args(q, k, v, nq, nk, heads, q_seg, q_t, k_seg, k_t, strength, window,
                          falloff, cap, scale, o, o_dtype, lse);
   const bool pen = strength > 0.f && cap > 0.f;
@@ -313,6 +334,7 @@ int route(const void* q, const void* k, const void* v, int dtype, int n, int hea
   if (!blocks_ok(n, block_size) || nb > router_max_blocks()) return H3_EUNSUPPORTED;
   const size_t need = router_ws_bytes(n, heads, head_dim, block_size, tail);
   if (!ws || ws_bytes < need) return H3_EWORKSPACE;
+  if (force_fail("router")) return H3_EFORCED;
   RouterWs w = router_ws_carve(ws, n, heads, head_dim, block_size, tail);
   hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, block_size,
                                seg, protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
@@ -341,6 +363,7 @@ int sparse(const void* q, const void* k, const void* v, int dtype, int n, int he
   const size_t base = attn_dense_tara_workspace(n, heads, head_dim, dtype);
   const size_t need = base + (int8qk ? int8_ws_bytes(n, heads, head_dim) : 0);
   if (need && (!ws || ws_bytes < need)) return H3_EWORKSPACE;
+  if (force_fail("sparse")) return H3_EFORCED;
   AttnArgs a = make_args(q, k, v, n, n, heads, seg, t, seg, t, strength, window, falloff, cap,
                          scale, o, o_dtype, lse);
   if (int8qk) {
@@ -491,6 +514,7 @@ int attn_dense_tara_via(const void* q, const void* k, const void* v, int dtype, 
   ViaPlan p;
   if (!plan_nothrow(seg_host, t_host, n, heads, head_dim, dtype, p)) return H3_ENOMEM;
   if (!ws || ws_bytes < p.total) return H3_EWORKSPACE;
+  if (force_fail("dense")) return H3_EFORCED;
 
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;

@@ -25,6 +25,15 @@
  * Errors     every argument check runs before any HIP call, so a bad call
  *            returns without touching the device. Nothing throws across the
  *            boundary.
+ * Forced     failure injection for a caller's dense fallback ("H3 SLA
+ * failures   Attention", "Install": when the sparse kernel fails, the run
+ *            degrades to plain dense attention). The environment variable
+ *            H3ATTN_FORCE_FAIL holds a comma-separated list of call families:
+ *            "dense" (attn_dense_tara, attn_dense_tara_via), "router" (the
+ *            attn_block_router* calls) and "sparse" (the attn_block_sparse*
+ *            calls). Entry points of a listed family return H3_EFORCED after
+ *            their argument checks and before any HIP call. It is read on
+ *            every call.
  */
 #ifndef H3ATTN_H
 #define H3ATTN_H
@@ -42,6 +51,7 @@ extern "C" {
 #define H3_ELAUNCH      (-3)  /* a kernel launch failed (hipGetLastError) */
 #define H3_EWORKSPACE   (-4)  /* workspace pointer null or smaller than required */
 #define H3_ENOMEM       (-5)  /* host memory for a call's plan could not be allocated */
+#define H3_EFORCED      (-6)  /* failure forced by H3ATTN_FORCE_FAIL (note above) */
 
 #define H3_DTYPE_F32  0
 #define H3_DTYPE_BF16 1

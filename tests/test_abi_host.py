@@ -44,7 +44,8 @@ def test_version_and_status_strings():
     assert "invalid" in api.status_string(-1)
     assert "workspace" in api.status_string(-4)
     assert "host memory" in api.status_string(api.H3_ENOMEM)
-    assert api.status_string(-6) == "unknown status"
+    assert "H3ATTN_FORCE_FAIL" in api.status_string(api.H3_EFORCED)
+    assert api.status_string(-7) == "unknown status"
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -319,3 +320,51 @@ def test_workspace_byte_count():
     assert api._nbytes(None) == 0
     assert api._nbytes(torch.zeros(10, dtype=torch.float32)) == 40
     assert api._nbytes(torch.zeros((3, 5), dtype=torch.uint8)) == 15
+
+
+# ------------------------------------------------------- forced failures (host)
+# Every call below carries valid arguments and a large enough workspace, with its
+# family listed in H3ATTN_FORCE_FAIL: the hook returns H3_EFORCED before the first HIP
+# call, so the placeholder pointers are never read.
+BIG = 1 << 40
+
+
+@pytest.mark.parametrize("env", ["dense", "router,dense", "sparse,dense"])
+def test_forced_failure_dense(monkeypatch, env):
+    monkeypatch.setenv("H3ATTN_FORCE_FAIL", env)
+    assert dense(ws=P, wsb=BIG) == api.H3_EFORCED
+    seg = np.zeros(300, dtype=np.uint8)
+    t = np.zeros(300, dtype=np.float32)
+    L = api.lib()
+    assert L.attn_dense_tara_via(P, P, P, 1, 300, 2, 128, P, P, api._np_ptr(seg),
+                                 api._np_ptr(t), 2.0, 0.2, 0.25, 6.0, 0.088, P, 1, P, P, BIG,
+                                 None) == api.H3_EFORCED
+
+
+@pytest.mark.parametrize("env", ["router", "sparse,router"])
+def test_forced_failure_router(monkeypatch, env):
+    monkeypatch.setenv("H3ATTN_FORCE_FAIL", env)
+    assert router(ws=P, wsb=BIG) == api.H3_EFORCED
+    assert api.lib().attn_block_router_tail(P, P, P, 1, 640, 2, 128, P, 64, 64, 3, 0.088, P, P,
+                                            2, P, P, P, BIG, None) == api.H3_EFORCED
+
+
+@pytest.mark.parametrize("env", ["sparse", "dense,sparse,router"])
+def test_forced_failure_sparse(monkeypatch, env):
+    monkeypatch.setenv("H3ATTN_FORCE_FAIL", env)
+    assert sparse(ws=P, wsb=BIG) == api.H3_EFORCED
+    L = api.lib()
+    args = (P, P, P, 1, 256, 2, 128, P, P, 2.0, 0.2, 0.25, 6.0, 0.088, 64, P, 2, P, 1)
+    assert L.attn_block_sparse_tail(*args, P, P, P, 1, P, P, BIG, None) == api.H3_EFORCED
+    assert L.attn_block_sparse_sinks(*args, None, None, 4, P, 1, P, P, BIG, None) == api.H3_EFORCED
+    assert L.attn_block_sparse_int8qk(*args, None, None, 0, P, 1, P, P, BIG,
+                                      None) == api.H3_EFORCED
+
+
+def test_forced_failure_still_validates_first(monkeypatch):
+    """Argument errors keep their own status when a failure is forced."""
+    monkeypatch.setenv("H3ATTN_FORCE_FAIL", "dense,router,sparse")
+    assert dense(q=None, ws=P, wsb=BIG) == api.H3_EINVAL
+    assert dense() == api.H3_EWORKSPACE
+    assert router(bs=16, ws=P, wsb=BIG) == api.H3_EUNSUPPORTED
+    assert sparse(ksel=-1, ws=P, wsb=BIG) == api.H3_EINVAL
