@@ -22,13 +22,16 @@ the identities above and brute force on small inputs.
 from .tara import (tara_penalty, tara_bias, dense_tara, plain_attention, lse_merge,
                    tara_partitions, runs)
 from .router import (router_plan, select_count, block_means_fp32, pooled_scores_fp32,
-                     select_topk, route_head)
+                     select_topk, route_head, reference_ranges, router_plan_ref, route_head_ref,
+                     REF_OFF, REF_LIGHT, REF_HEAVY, LIGHT_REFERENCE_SPARSITY)
 from .sparse import block_sparse_block, block_sparse, tail_terms, is_sink_block
 from .quant import quantize_int8, dequantize_int8, int8_roundtrip
 
 __all__ = [
     "tara_penalty", "tara_bias", "dense_tara", "plain_attention", "lse_merge",
     "tara_partitions", "runs", "router_plan", "select_count", "block_means_fp32",
-    "pooled_scores_fp32", "select_topk", "route_head", "block_sparse_block", "block_sparse",
+    "pooled_scores_fp32", "select_topk", "route_head", "reference_ranges", "router_plan_ref",
+    "route_head_ref", "REF_OFF", "REF_LIGHT", "REF_HEAVY", "LIGHT_REFERENCE_SPARSITY",
+    "block_sparse_block", "block_sparse",
     "tail_terms", "is_sink_block", "quantize_int8", "dequantize_int8", "int8_roundtrip",
 ]

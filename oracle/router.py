@@ -23,6 +23,17 @@ Readings where the pages are silent (each listed in the design notes):
   chosen tiles are reported in ascending tile order;
 - every query block is routed (text and audio query blocks included), each
   head separately.
+
+Reference protection ("H3 SLA Attention", inputs table, reference_protection; the guide
+video is the visual reference of the packed sequence):
+- Off: no quota; reference tiles compete in the ordinary top-k.
+- Heavy: every video tile that holds a guide row is protected (attended by every query
+  block); the ordinary top-k runs over the remaining video tiles.
+- Light: the ordinary top-k over all video tiles, and in addition, for each reference
+  range (a maximal run of video tiles with consecutive block indices that hold a guide
+  row), the best-scoring tiles of that range at a fixed reference sparsity of 0.85, i.e.
+  select_count(n_range, 0.85) tiles. A query block attends the union; sparsity 0 still
+  routes every tile.
 """
 from __future__ import annotations
 
@@ -132,3 +143,72 @@ def route_head(q32_h, k32_h, seg, protected_prefix_len, block_size, k):
     kbar = block_means_fp32(k32_h, block_size)
     scores = pooled_scores_fp32(qbar, kbar[video])
     return select_topk(scores, video, k)
+
+
+REF_OFF, REF_LIGHT, REF_HEAVY = 0, 1, 2
+LIGHT_REFERENCE_SPARSITY = 0.85
+
+
+def reference_ranges(seg, protected_prefix_len, block_size):
+    """Video tiles that hold a guide (visual reference) row, as ranges of consecutive
+    block indices: a list of arrays of block indices, in ascending order."""
+    seg = np.asarray(seg)
+    n = len(seg)
+    _, _, video, _ = router_plan(seg, protected_prefix_len, block_size, 0.0)
+    ref = [int(b) for b in video
+           if np.any(seg[b * block_size:min(n, (b + 1) * block_size)] == SEG_GUIDE)]
+    ranges = []
+    for b in ref:
+        if ranges and ranges[-1][-1] == b - 1:
+            ranges[-1].append(b)
+        else:
+            ranges.append([b])
+    return [np.array(r, dtype=np.int64) for r in ranges]
+
+
+def router_plan_ref(seg, protected_prefix_len, block_size, sparsity, mode):
+    """Routing plan under a reference-protection mode.
+
+    Returns (nb, protected blocks, routed-candidate video tiles, k, quotas): k is the
+    ordinary top-k count over the candidates, and quotas a list of (range tiles, count)
+    guaranteed per reference range (Light only). The tile-list width a query block
+    needs is k + the sum of the quota counts.
+    """
+    nb, prot, video, k = router_plan(seg, protected_prefix_len, block_size, sparsity)
+    if mode == REF_OFF:
+        return nb, prot, video, k, []
+    ranges = reference_ranges(seg, protected_prefix_len, block_size)
+    if mode == REF_HEAVY:
+        ref = set(int(b) for r in ranges for b in r)
+        prot = np.array(sorted(set(prot.tolist()) | ref), dtype=np.int64)
+        video = np.array([b for b in video if int(b) not in ref], dtype=np.int64)
+        return nb, prot, video, select_count(len(video), sparsity), []
+    if mode == REF_LIGHT:
+        quotas = [(r, select_count(len(r), LIGHT_REFERENCE_SPARSITY)) for r in ranges]
+        return nb, prot, video, k, quotas
+    raise ValueError(f"unknown reference-protection mode {mode}")
+
+
+def route_head_ref(q32_h, k32_h, seg, protected_prefix_len, block_size, sparsity, mode):
+    """Routing of one head under a reference-protection mode: per query block, the
+    ascending union of the ordinary top-k over the candidate video tiles and (Light)
+    each reference range's quota of its best-scoring tiles, padded with -1 to the
+    list width k + sum of quotas. Returns [nqb, width] int64."""
+    nb, _, video, k, quotas = router_plan_ref(seg, protected_prefix_len, block_size,
+                                              sparsity, mode)
+    width = k + sum(c for _, c in quotas)
+    qbar = block_means_fp32(q32_h, block_size)
+    kbar = block_means_fp32(k32_h, block_size)
+    chosen = [set() for _ in range(nb)]
+    parts = [(video, k)] + list(quotas)
+    for tiles, count in parts:
+        if count == 0 or len(tiles) == 0:
+            continue
+        picked = select_topk(pooled_scores_fp32(qbar, kbar[tiles]), tiles, count)
+        for qb in range(nb):
+            chosen[qb].update(int(b) for b in picked[qb])
+    out = np.full((nb, width), -1, dtype=np.int64)
+    for qb in range(nb):
+        row = sorted(chosen[qb])
+        out[qb, :len(row)] = row
+    return out

@@ -464,6 +464,170 @@ def test_route_head_pin_catches_planted_mistakes():
     assert not np.array_equal(every_block, want)
 
 
+def _brute_route_ref(q32, k32, seg, prefix, bs, sparsity, mode):
+    """Reference-protected routing written out with scalar loops ("H3 SLA Attention",
+    inputs table, reference_protection): video tiles and reference ranges from a row
+    scan, the pooled scores as in _brute_route, pairwise ranks inside each candidate
+    group; Light adds each range's best ceil(0.15 n - 1e-9) tiles (at least one) to the
+    ordinary top-k, Heavy protects the reference tiles and ranks the others."""
+    n, d = q32.shape
+    nb = (n + bs - 1) // bs
+    rows = lambda b: range(b * bs, min(n, b * bs + bs))
+    video = [b for b in range(nb) if not (b * bs < prefix or any(
+        int(seg[r]) in (W.SEG_TEXT, W.SEG_AUDIO) for r in rows(b)))]
+    ref = [b for b in video if any(int(seg[r]) == W.SEG_GUIDE for r in rows(b))]
+    ranges = []
+    for b in ref:
+        if ranges and ranges[-1][-1] == b - 1:
+            ranges[-1].append(b)
+        else:
+            ranges.append([b])
+
+    def count(m, s):
+        if m == 0:
+            return 0
+        return m if s == 0.0 else min(m, max(1, math.ceil((1.0 - s) * m - 1e-9)))
+
+    cand = [b for b in video if b not in ref] if mode == oracle.REF_HEAVY else video
+    groups = [(cand, count(len(cand), sparsity))]
+    if mode == oracle.REF_LIGHT:
+        groups += [(r, count(len(r), 0.85)) for r in ranges]
+    width = sum(c for _, c in groups)
+
+    def mean(x, b):
+        out = []
+        for c in range(d):
+            acc = np.float32(0.0)
+            for r in rows(b):
+                acc = np.float32(acc + x[r, c])
+            out.append(np.float32(acc / np.float32(len(rows(b)))))
+        return out
+
+    qbar = [mean(q32, b) for b in range(nb)]
+    kbar = {b: mean(k32, b) for b in video}
+    out = np.full((nb, width), -1, dtype=np.int64)
+    for qb in range(nb):
+        score = {}
+        for kb in video:
+            acc = np.float32(0.0)
+            for c in range(d):
+                acc = np.float32(acc + np.float32(qbar[qb][c] * kbar[kb][c]))
+            score[kb] = float(acc)
+        chosen = set()
+        for tiles, kk in groups:
+            chosen |= {kb for kb in tiles if sum(
+                1 for j in tiles if score[j] > score[kb] or (score[j] == score[kb] and j < kb)) < kk}
+        row = sorted(chosen)
+        out[qb, :len(row)] = row
+    return out
+
+
+def _ref_case(seed=23):
+    """Blocks of 4 rows: text, two guide spans (10 and 7 blocks, the second split off by
+    a text block), audio, output video; the guide key means score highest."""
+    rng = np.random.default_rng(seed)
+    seg = np.array([0] * 4 + [1] * 40 + [0] * 4 + [1] * 28 + [2] * 4 + [3] * 37, dtype=np.uint8)
+    q32 = rng.standard_normal((len(seg), 5)).astype(np.float32)
+    k32 = rng.standard_normal((len(seg), 5)).astype(np.float32)
+    k32[seg == 1] += 0.5
+    return seg, q32, k32
+
+
+def test_reference_ranges_and_plan_full_scale():
+    """Full scale, block 64: the guide span gives one reference range, blocks 114-961
+    (block 113 holds text rows, block 962 audio rows); Light guarantees
+    ceil(0.15 * 848) = 128 of them; Heavy protects all 848 and routes the 849 output
+    tiles."""
+    wl = W.FULL_SPARSE
+    seg, _ = W.layout(wl)
+    ranges = oracle.reference_ranges(seg, wl.protected_prefix_len, 64)
+    assert len(ranges) == 1 and ranges[0][0] == 114 and ranges[0][-1] == 961
+    assert len(ranges[0]) == 848
+    nb, prot, video, k, quotas = oracle.router_plan_ref(seg, wl.protected_prefix_len, 64, 0.9,
+                                                        oracle.REF_LIGHT)
+    assert (nb, len(prot), len(video), k) == (1827, 130, 1697, 170)
+    assert [c for _, c in quotas] == [128]
+    nb, prot, video, k, quotas = oracle.router_plan_ref(seg, wl.protected_prefix_len, 64, 0.9,
+                                                        oracle.REF_HEAVY)
+    assert (len(prot), len(video), k, quotas) == (978, 849, 85, [])
+    guide_blocks = {r // 64 for r in np.nonzero(seg == W.SEG_GUIDE)[0]}
+    assert guide_blocks <= set(prot.tolist())
+    assert oracle.router_plan_ref(seg, wl.protected_prefix_len, 64, 0.9, oracle.REF_OFF)[3] == 170
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_route_head_ref_brute_force_tiny(mode):
+    """route_head_ref equals the scalar brute force at several sparsities and prefixes,
+    for Light (two reference ranges) and Heavy."""
+    seg, q32, k32 = _ref_case()
+    for prefix in (0, 4, 9):
+        for s in (0.0, 0.5, 0.8, 0.95):
+            got = oracle.route_head_ref(q32, k32, seg, prefix, 4, s, mode)
+            assert np.array_equal(got, _brute_route_ref(q32, k32, seg, prefix, 4, s, mode)), \
+                (mode, prefix, s)
+
+
+def test_reference_protection_invariants():
+    """Off equals route_head; Light lists contain the Off lists and each range's quota of
+    best tiles; at sparsity 0 every mode attends every block (so the sparse result is
+    dense); Heavy never routes a reference tile, which it protects instead."""
+    seg, q32, k32 = _ref_case(29)
+    prefix = 4
+    nb, _, video, _ = oracle.router_plan(seg, prefix, 4, 0.0)
+    ranges = oracle.reference_ranges(seg, prefix, 4)
+    assert [len(r) for r in ranges] == [10, 7]
+    for s in (0.3, 0.9):
+        k = oracle.select_count(len(video), s)
+        off = oracle.route_head(q32, k32, seg, prefix, 4, k)
+        assert np.array_equal(oracle.route_head_ref(q32, k32, seg, prefix, 4, s, oracle.REF_OFF),
+                              off)
+        light = oracle.route_head_ref(q32, k32, seg, prefix, 4, s, oracle.REF_LIGHT)
+        assert light.shape[1] == k + 2 + 2          # quotas ceil(1.5) and ceil(1.05)
+        qbar = oracle.block_means_fp32(q32, 4)
+        kbar = oracle.block_means_fp32(k32, 4)
+        for qb in range(nb):
+            row = set(light[qb][light[qb] >= 0].tolist())
+            assert set(off[qb].tolist()) <= row
+            for r in ranges:
+                best = oracle.select_topk(oracle.pooled_scores_fp32(qbar[qb:qb + 1], kbar[r]), r,
+                                          oracle.select_count(len(r), 0.85))[0]
+                assert set(best.tolist()) <= row
+        heavy = oracle.route_head_ref(q32, k32, seg, prefix, 4, s, oracle.REF_HEAVY)
+        ref_tiles = {int(b) for r in ranges for b in r}
+        assert ref_tiles.isdisjoint(set(heavy.ravel().tolist()))
+    for mode in (oracle.REF_OFF, oracle.REF_LIGHT, oracle.REF_HEAVY):
+        _, prot, _, _, _ = oracle.router_plan_ref(seg, prefix, 4, 0.0, mode)
+        lists = oracle.route_head_ref(q32, k32, seg, prefix, 4, 0.0, mode)
+        for qb in range(nb):
+            assert set(lists[qb].tolist()) - {-1} | set(prot.tolist()) == set(range(nb))
+
+
+def test_reference_pin_catches_planted_mistakes(monkeypatch):
+    """A Light quota taken at the call's sparsity instead of 0.85, and a Heavy mode that
+    leaves the reference tiles among the routed candidates, both fail the brute force."""
+    seg, q32, k32 = _ref_case()
+    want_l = _brute_route_ref(q32, k32, seg, 4, 4, 0.95, oracle.REF_LIGHT)
+    want_h = _brute_route_ref(q32, k32, seg, 4, 4, 0.8, oracle.REF_HEAVY)
+    monkeypatch.setattr(orouter, "LIGHT_REFERENCE_SPARSITY", 0.95)
+    assert not np.array_equal(oracle.route_head_ref(q32, k32, seg, 4, 4, 0.95, oracle.REF_LIGHT),
+                              want_l)
+    monkeypatch.undo()
+    good_plan = orouter.router_plan_ref
+
+    def heavy_keeps_candidates(seg_, prefix_, bs_, s_, mode_):
+        nb, prot, video, k, quotas = good_plan(seg_, prefix_, bs_, s_, mode_)
+        if mode_ == oracle.REF_HEAVY:
+            _, _, video, _ = orouter.router_plan(seg_, prefix_, bs_, s_)
+            k = orouter.select_count(len(video), s_)
+        return nb, prot, video, k, quotas
+
+    monkeypatch.setattr(orouter, "router_plan_ref", heavy_keeps_candidates)
+    assert not np.array_equal(orouter.route_head_ref(q32, k32, seg, 4, 4, 0.8, oracle.REF_HEAVY),
+                              want_h)
+    monkeypatch.undo()
+    assert np.array_equal(oracle.route_head_ref(q32, k32, seg, 4, 4, 0.8, oracle.REF_HEAVY), want_h)
+
+
 # -------------------------------------------------------------- sparse pins
 
 def _sparse_case(seed=300, strength=2.0):
