@@ -471,6 +471,25 @@ def main():
         del ws_i8
         print("# int8 QK done", file=sys.stderr, flush=True)
 
+        # reference-protection quota on the guide span (Light: the best 15% of the guide
+        # tiles on top of the ordinary top-k; Heavy: every guide tile protected)
+        for mode, name in ((api.H3_REF_LIGHT, "light"), (api.H3_REF_HEAVY, "heavy")):
+            pr_ = api.router_plan_ref(seg, wl.protected_prefix_len, args.sparsity, mode)
+            tr_ = torch.empty((H, nb, pr_["k_sel"]), dtype=torch.int32, device="cuda")
+            pp_ = torch.empty((pr_["n_prot"],), dtype=torch.int32, device="cuda")
+            row = time_pair(
+                lambda: api.attn_block_router_ref(qd, kd, segd, seg, wl.protected_prefix_len,
+                                                  args.sparsity, mode, tiles=tr_, prot=pp_,
+                                                  ws=ws_router),
+                lambda: api.attn_block_sparse(qd, kd, vd, segd, td, tr_, pp_, *tara,
+                                              scale=scale, o=o_sparse, lse=l_sparse,
+                                              ws=ws_dense))
+            row.update({"sparsity": args.sparsity, "block_size": 64, "list_width": pr_["k_sel"],
+                        "n_prot": pr_["n_prot"]})
+            next_rows[f"reference_protection_{name}"] = row
+            del tr_, pp_
+        print("# reference protection done", file=sys.stderr, flush=True)
+
     roofline = None
     if d:
         traffic = None

@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(_PKG, "libh3attn.so")
 H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE, H3_ENOMEM = 0, -1, -2, -3, -4, -5
 H3_EFORCED = -6
 H3_DTYPE_F32, H3_DTYPE_BF16 = 0, 1
+H3_REF_OFF, H3_REF_LIGHT, H3_REF_HEAVY = 0, 1, 2
 
 EXPORTS = (
     "h3attn_version", "h3attn_status_string",
     "attn_dense_tara_workspace", "attn_dense_tara",
     "attn_router_plan", "attn_block_router_workspace", "attn_block_router",
+    "attn_router_plan_ref", "attn_block_router_ref",
     "attn_block_sparse_workspace", "attn_block_sparse",
     "attn_block_router_tail_workspace", "attn_block_router_tail", "attn_block_sparse_tail",
     "attn_block_sparse_sinks",
@@ -42,6 +44,9 @@ _SIGS = {
                              _f, _f, _f, _f, _f, _vp, _i, _vp, _vp, _sz, _vp]),
     "attn_router_plan": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "attn_block_router_workspace": (_sz, [_i, _i, _i, _i]),
+    "attn_router_plan_ref": (_i, [_vp, _i, _i, _i, _d, _i, _vp, _vp, _vp, _vp]),
+    "attn_block_router_ref": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _i, _d, _i, _i, _vp,
+                                   _vp, _i, _vp, _sz, _vp]),
     "attn_block_router": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i,
                                _vp, _sz, _vp]),
     "attn_block_sparse_workspace": (_sz, [_i, _i, _i, _i]),
@@ -229,6 +234,53 @@ def router_plan(seg_host, protected_prefix_len, sparsity_ratio, block_size=64):
     _check("attn_router_plan", st)
     nb, nv, npr, k = (x.value for x in outs)
     return {"nb": nb, "n_video": nv, "n_prot": npr, "k_sel": k}
+
+
+def router_plan_ref(seg_host, protected_prefix_len, sparsity_ratio, reference_protection,
+                    block_size=64):
+    """Host-only routing plan under a reference-protection mode: dict(nb, n_video, n_prot,
+    k_sel), k_sel being the list width."""
+    seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+    outs = [ctypes.c_int(0) for _ in range(4)]
+    st = lib().attn_router_plan_ref(_np_ptr(seg_host), len(seg_host), protected_prefix_len,
+                                    block_size, float(sparsity_ratio), int(reference_protection),
+                                    *[ctypes.byref(x) for x in outs])
+    _check("attn_router_plan_ref", st)
+    nb, nv, npr, k = (x.value for x in outs)
+    return {"nb": nb, "n_video": nv, "n_prot": npr, "k_sel": k}
+
+
+def attn_block_router_ref(q, k, seg, seg_host, protected_prefix_len, sparsity_ratio,
+                          reference_protection, block_size=64, tiles=None, prot=None, ws=None,
+                          stream=None):
+    """Pooled router with reference protection: returns (tiles int32 [H, nb, k_sel], prot
+    int32 [n_prot]) with the plan's list width k_sel."""
+    import torch
+    n, H, D = q.shape
+    seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+    if len(seg_host) != n:
+        raise ValueError(f"attn_block_router_ref: seg_host needs {n} rows")
+    plan = router_plan_ref(seg_host, protected_prefix_len, sparsity_ratio, reference_protection,
+                           block_size)
+    nb, k_sel, n_prot = plan["nb"], plan["k_sel"], plan["n_prot"]
+    if tiles is None:
+        tiles = torch.empty((H, nb, k_sel), dtype=torch.int32, device=q.device)
+    if prot is None:
+        prot = torch.empty((n_prot,), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = _workspace(router_workspace_bytes(n, H, D, block_size), q.device)
+    T = _dt()
+    _check_args("attn_block_router_ref", q, [
+        ("k", k, (n, H, D), (q.dtype,)), ("seg", seg, (n,), T["u8"]),
+        ("tiles", tiles, (H, nb, k_sel), T["i32"]), ("prot", prot, (n_prot,), T["i32"])], ws)
+    st = lib().attn_block_router_ref(_ptr(q), _ptr(k), _dtype_code(q), n, H, D, _ptr(seg),
+                                     _np_ptr(seg_host), protected_prefix_len, block_size,
+                                     float(sparsity_ratio), int(reference_protection), k_sel,
+                                     _ptr(tiles) if k_sel > 0 else None,
+                                     _ptr(prot) if n_prot > 0 else None, n_prot,
+                                     _ptr(ws), _nbytes(ws), _stream(stream))
+    _check("attn_block_router_ref", st)
+    return tiles, prot
 
 
 def router_workspace_bytes(n, heads, head_dim, block_size=64):

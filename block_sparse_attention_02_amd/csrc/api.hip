@@ -303,6 +303,95 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
   return H3_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host plan of the routed lists under a reference-protection mode ("H3 SLA Attention",
+// inputs table, reference_protection): the protected / candidate counts, the ordinary
+// routed count, and for Light the reference ranges (maximal runs of video tiles with
+// consecutive block indices holding a guide row) with their positions in the video-tile
+// list and guaranteed counts at the fixed reference sparsity 0.85.
+constexpr double kLightReferenceSparsity = 0.85;
+
+int select_count(int m, double s) {
+  if (m <= 0) return 0;
+  if (s == 0.0) return m;
+  const int k = (int)std::ceil((1.0 - s) * (double)m - 1e-9);
+  return std::min(m, std::max(1, k));
+}
+
+struct RefPlan {
+  int nb = 0, n_prot = 0, n_cand = 0, k_ord = 0, width = 0, n_ranges = 0;
+  RefQuota rq{};
+};
+
+// Returns H3_OK, H3_EINVAL or H3_EUNSUPPORTED (block size, mode, or more than
+// kMaxRefRanges reference ranges in Light mode).
+int plan_ref(const uint8_t* seg, int n, int prefix, int bs, double s, int mode, RefPlan& p) {
+  if (!seg || n <= 0 || prefix < 0 || prefix > n) return H3_EINVAL;
+  if (!std::isfinite(s) || s < 0.0 || s >= 1.0) return H3_EINVAL;
+  if (!bs_ok(bs)) return H3_EUNSUPPORTED;
+  if (mode != H3_REF_OFF && mode != H3_REF_LIGHT && mode != H3_REF_HEAVY)
+    return H3_EUNSUPPORTED;
+  p = RefPlan{};
+  p.nb = (n + bs - 1) / bs;
+  int vpos = 0, prev_ref = -2;
+  for (int b = 0; b < p.nb; ++b) {
+    const int lo = b * bs, hi = std::min(n, lo + bs);
+    bool text_audio = lo < prefix, guide = false;
+    for (int r = lo; r < hi; ++r) {
+      text_audio = text_audio || seg[r] == H3_SEG_TEXT || seg[r] == H3_SEG_AUDIO;
+      guide = guide || seg[r] == H3_SEG_GUIDE;
+    }
+    const bool ref = !text_audio && guide;
+    if (text_audio || (mode == H3_REF_HEAVY && ref)) {
+      ++p.n_prot;
+      continue;
+    }
+    if (mode == H3_REF_LIGHT && ref) {  // a reference range starts or goes on
+      if (prev_ref != b - 1) {
+        if (p.n_ranges == kMaxRefRanges) return H3_EUNSUPPORTED;
+        p.rq.lo[p.n_ranges] = vpos;
+        p.rq.hi[p.n_ranges] = vpos;
+        ++p.n_ranges;
+      }
+      ++p.rq.hi[p.n_ranges - 1];
+      prev_ref = b;
+    }
+    ++vpos;
+  }
+  p.n_cand = vpos;
+  p.k_ord = select_count(p.n_cand, s);
+  p.width = p.k_ord;
+  p.rq.k_ord = p.k_ord;
+  p.rq.n = p.n_ranges;
+  for (int j = 0; j < p.n_ranges; ++j) {
+    p.rq.q[j] = select_count(p.rq.hi[j] - p.rq.lo[j], kLightReferenceSparsity);
+    p.width += p.rq.q[j];
+  }
+  p.width = std::min(p.width, p.n_cand);  // a union never exceeds the candidates
+  return H3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_router_plan_ref(const uint8_t* seg_host, int n, int protected_prefix_len,
+                         int block_size, double sparsity_ratio, int reference_protection,
+                         int* nb, int* n_video, int* n_prot, int* k_sel) {
+  RefPlan p;
+  if (int st = plan_ref(seg_host, n, protected_prefix_len, block_size, sparsity_ratio,
+                        reference_protection, p))
+    return st;
+  if (nb) *nb = p.nb;
+  if (n_video) *n_video = p.n_cand;
+  if (n_prot) *n_prot = p.n_prot;
+  if (k_sel) *k_sel = p.width;
+  return H3_OK;
+}
+
 size_t attn_block_router_workspace(int n, int heads, int head_dim, int block_size) {
   if (n <= 0 || heads <= 0 || !dim_ok(head_dim) || !bs_ok(block_size)) return 0;
   return router_ws_bytes(n, heads, head_dim, block_size, false);
@@ -320,7 +409,8 @@ namespace {
 int route(const void* q, const void* k, const void* v, int dtype, int n, int heads,
           int head_dim, const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
           int32_t* tiles, int32_t* prot, int n_prot, bool tail, float scale, float* tail_lse,
-          float* tail_v, void* ws, size_t ws_bytes, void* stream) {
+          float* tail_v, void* ws, size_t ws_bytes, void* stream,
+          bool guide_protected = false, const RefQuota* rq = nullptr) {
   if (!q || !k || !seg || n <= 0 || heads <= 0) return H3_EINVAL;
   if (tail && (!v || !tail_lse || !tail_v || !std::isfinite(scale) || !(scale > 0.f)))
     return H3_EINVAL;
@@ -339,7 +429,7 @@ int route(const void* q, const void* k, const void* v, int dtype, int n, int hea
   hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, block_size,
                                seg, protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
                                tail ? tail_lse : nullptr, tail ? tail_v : nullptr,
-                               (hipStream_t)stream);
+                               (hipStream_t)stream, guide_protected, rq);
   return e == hipSuccess ? H3_OK : H3_ELAUNCH;
 }
 
@@ -412,6 +502,23 @@ int attn_block_router_tail(const void* q, const void* k, const void* v, int dtyp
                            void* stream) {
   return route(q, k, v, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size, k_sel,
                tiles, prot, n_prot, true, scale, tail_lse, tail_v, ws, ws_bytes, stream);
+}
+
+int attn_block_router_ref(const void* q, const void* k, int dtype, int n, int heads,
+                          int head_dim, const uint8_t* seg, const uint8_t* seg_host,
+                          int protected_prefix_len, int block_size, double sparsity_ratio,
+                          int reference_protection, int k_sel, int32_t* tiles, int32_t* prot,
+                          int n_prot, void* ws, size_t ws_bytes, void* stream) {
+  if (!seg_host) return H3_EINVAL;
+  RefPlan p;
+  if (int st = plan_ref(seg_host, n, protected_prefix_len, block_size, sparsity_ratio,
+                        reference_protection, p))
+    return st;
+  if (k_sel != p.width) return H3_EINVAL;  // the list width of this plan, no truncation
+  const bool light = reference_protection == H3_REF_LIGHT;
+  return route(q, k, nullptr, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size,
+               k_sel, tiles, prot, n_prot, false, 0.f, nullptr, nullptr, ws, ws_bytes, stream,
+               reference_protection == H3_REF_HEAVY, light ? &p.rq : nullptr);
 }
 
 size_t attn_block_sparse_workspace(int n, int heads, int head_dim, int dtype) {

@@ -103,13 +103,26 @@ struct TailArgs {
   float* wts;          // [H][nb][nbp] normalised weights of the unrouted video tiles
   int nbp;
 };
+// Light reference protection (see router.hip): the ordinary routed count and, per
+// reference range, its position in the video-tile list and its guaranteed count.
+constexpr int kMaxRefRanges = 16;
+struct RefQuota {
+  int k_ord;                  // ordinary top-k over all video tiles
+  int n;                      // reference ranges
+  int lo[kMaxRefRanges];      // first position of the range in the video-tile list
+  int hi[kMaxRefRanges];      // one past its last position
+  int q[kMaxRefRanges];       // tiles of the range guaranteed to every query block
+};
 size_t router_ws_bytes(int n, int H, int D, int bs, bool tail);
 RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail);
 int router_max_blocks();
+// guide_protected: Heavy reference protection (every block holding a guide row is
+// protected); rq: Light reference quota, or null.
 hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
                          int D, int bs, const uint8_t* seg, int prefix, int k_sel,
                          int32_t* tiles, int32_t* prot, int prot_cap, const RouterWs& w,
-                         float scale, float* tail_lse, float* tail_v, hipStream_t s);
+                         float scale, float* tail_lse, float* tail_v, hipStream_t s,
+                         bool guide_protected = false, const RefQuota* rq = nullptr);
 
 // LSE merge and accumulator finalisation.
 hipError_t launch_lse_merge(float* o_acc, float* lse_acc, const float* o_i, const float* lse_i,

@@ -21,6 +21,8 @@
 // query block into one pooled key: logit ln sum_u n_u exp(scale * S[qb,u]) from the same
 // float32 pooled scores, and normalised weights whose product with the V means (float32
 // on the matrix cores) gives the key's value.
+#include <atomic>
+
 #include "h3_internal.h"
 
 #pragma clang fp contract(off)
@@ -36,7 +38,7 @@ constexpr int kTopkWaves = 4;
 // ------------------------------------------------------------------ 1. flags
 __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __restrict__ seg,
                                                             int n, int prefix, int nb,
-                                                            int bs,
+                                                            int bs, bool guide_protected,
                                                             int32_t* __restrict__ prot,
                                                             int prot_cap,
                                                             int32_t* __restrict__ video,
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __res
       isp = lo < prefix;
       for (int r = lo; r < hi && !isp; ++r) {
         const int s = seg[r];
-        isp = (s == kSegText) || (s == kSegAudio);
+        isp = (s == kSegText) || (s == kSegAudio) || (guide_protected && s == kSegGuide);
       }
     }
     const bool isv = valid && !isp;
@@ -181,17 +183,20 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D, int QB, bool TAIL>
+template <int D, int QB, bool TAIL, bool REF = false>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar,
                                                           const int32_t* __restrict__ video,
                                                           const int32_t* __restrict__ counts,
                                                           int nb, int k_sel,
                                                           int32_t* __restrict__ tiles,
-                                                          TailArgs tail) {
+                                                          TailArgs tail, RefQuota rq) {
   static_assert(QB == 1 || QB == 4, "query blocks per workgroup");
+  static_assert(!(TAIL && REF), "the tail term is not combined with the reference quota");
   extern __shared__ float sc[];  // [QB][nv] pooled scores
   __shared__ int hist[kTopkWaves][256];
+  // reference quota: the union of the selections of each query block, one bit per block
+  __shared__ uint32_t chosen[REF ? QB : 1][REF ? kBitmapWords : 1];
   const int h = blockIdx.y;
   const int qb0 = blockIdx.x * QB;
   const int tid = threadIdx.x;
@@ -224,9 +229,106 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
   __syncthreads();
 
-  // ---- exact selection: radix select of the k-th best key, 8 bits per pass
   const bool active = w < QB;
   const float* my = sc + (active ? w : 0) * nv;
+  if constexpr (REF) {
+    // Light reference protection: the ordinary top-k over every video tile, then each
+    // reference range's quota of its best tiles (a contiguous run [lo, hi) of the
+    // video list), all marked in one bitmap per query block; the union is written in
+    // ascending block order and padded with -1 up to the list width k_sel.
+    for (int i = tid; i < QB * kBitmapWords; i += 256) (&chosen[0][0])[i] = 0u;
+    __syncthreads();
+    const int nparts = 1 + rq.n;
+    for (int part = 0; part < nparts; ++part) {
+      const int lo = part ? min(rq.lo[part - 1], nv) : 0;
+      const int hi = part ? min(rq.hi[part - 1], nv) : nv;
+      const int cnt = hi - lo;
+      const int kk = min(part ? rq.q[part - 1] : rq.k_ord, cnt);
+      if (kk <= 0) continue;  // workgroup-uniform
+      const bool all = kk == cnt;
+      uint32_t prefix = 0u, pmask = 0u;
+      int rem = kk;
+      for (int pass = 0; pass < 4 && !all; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int j = lane; j < 256; j += 64) hist[w][j] = 0;
+        __syncthreads();
+        if (active) {
+          for (int i = lo + lane; i < hi; i += 64) {
+            const uint32_t key = order_key(my[i]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[w][(key >> shift) & 255u], 1);
+          }
+        }
+        __syncthreads();
+        if (active) {
+          int c[4];
+          int sum = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { c[j] = hist[w][255 - 4 * lane - j]; sum += c[j]; }
+          int incl = sum;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+          }
+          const int excl = incl - sum;
+          const bool here = excl < rem && rem <= incl;
+          int digit = 0, above = 0;
+          if (here) {
+            int cum = excl;
+            for (int j = 0; j < 4; ++j) {
+              if (cum + c[j] >= rem) { digit = 255 - 4 * lane - j; above = cum; break; }
+              cum += c[j];
+            }
+          }
+          const uint64_t bm = __ballot(here);
+          const int src = __ffsll((unsigned long long)bm) - 1;
+          digit = __shfl(digit, src);
+          above = __shfl(above, src);
+          rem -= above;
+          prefix |= (uint32_t)digit << shift;
+          pmask |= 0xFFu << shift;
+        }
+        __syncthreads();
+      }
+      if (active) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int eq_seen = 0;
+        for (int base = lo; base < hi; base += 64) {
+          const int i = base + lane;
+          const bool valid = i < hi;
+          const uint32_t key = valid ? order_key(my[i]) : 0u;
+          const bool gt = valid && (all || key > prefix);
+          const bool eq = valid && !all && key == prefix;
+          const uint64_t eqm = __ballot(eq);
+          const bool sel = gt || (eq && eq_seen + __popcll(eqm & below) < rem);
+          if (sel) {
+            const int kb = video[i];
+            atomicOr(&chosen[w][kb >> 5], 1u << (kb & 31));
+          }
+          eq_seen += __popcll(eqm);
+        }
+      }
+    }
+    __syncthreads();
+    const int qb = qb0 + w;
+    if (active && qb < nb && k_sel > 0) {
+      int32_t* out = tiles + ((int64_t)h * nb + qb) * k_sel;
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      int pos = 0;
+      for (int base = 0; base < nb; base += 64) {
+        const int kb = base + lane;
+        const bool sel = kb < nb && ((chosen[w][kb >> 5] >> (kb & 31)) & 1u);
+        const uint64_t selm = __ballot(sel);
+        const int at = pos + __popcll(selm & below);
+        if (sel && at < k_sel) out[at] = kb;
+        pos += __popcll(selm);
+      }
+      for (int j = pos + lane; j < k_sel; j += 64) out[j] = -1;
+    }
+    return;
+  }
+
+  // ---- exact selection: radix select of the k-th best key, 8 bits per pass
   const int kk = min(k_sel, nv);
   const bool take_all = (kk == nv);
   uint32_t prefix = 0u, pmask = 0u;
@@ -459,17 +561,37 @@ RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
 // Largest block count the score/top-k kernel keeps in LDS (QB x nb floats).
 int router_max_blocks() { return kMaxBlocks; }
 
-template <int D, int QB, bool TAIL>
+// The device's LDS limit per workgroup, queried once per device (64 KB if the query
+// fails). The cache only ever holds that attribute, so concurrent first calls store the
+// same value.
+int max_lds_per_block() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 64 * 1024;
+  if (dev < kDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      v <= 0)
+    v = 64 * 1024;
+  if (dev < kDevices) cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+template <int D, int QB, bool TAIL, bool REF>
 void launch_topk(dim3 grid, size_t lds, hipStream_t s, const RouterWs& w, int nb, int k_sel,
-                 int32_t* tiles, const TailArgs& ta) {
-  router_topk_kernel<D, QB, TAIL><<<grid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts, nb,
-                                                         k_sel, tiles, ta);
+                 int32_t* tiles, const TailArgs& ta, const RefQuota& rq) {
+  router_topk_kernel<D, QB, TAIL, REF><<<grid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts,
+                                                              nb, k_sel, tiles, ta, rq);
 }
 
 template <int D, bool TAIL>
 void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, int n, int H,
                       int nb, int bs, int k_sel, int32_t* tiles, const RouterWs& w,
-                      const TailArgs& ta, hipStream_t s) {
+                      const TailArgs& ta, const RefQuota* rq, hipStream_t s) {
   const int chunks = (H * D / 8 + 127) / 128;
   dim3 pgrid(nb, chunks);
   if (bf16)
@@ -478,23 +600,29 @@ void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, in
   else
     router_pool_kernel<false, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, bs, w.qbar,
                                                               w.kbar, w.vbar);
-  // four query blocks per workgroup when their scores fit in this device's LDS next to
-  // the kernel's own arrays (about 12 KB)
-  int dev = 0, max_lds = 64 * 1024;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-          hipSuccess)
-    max_lds = 64 * 1024;
-  const bool wide = (size_t)4 * nb * sizeof(float) + 12 * 1024 <= (size_t)max_lds;
+  // four query blocks per workgroup when their scores fit in the LDS next to the
+  // kernel's own arrays (about 12 KB, and 4 bitmaps of the reference quota)
+  const size_t own = 12 * 1024 + (rq ? (size_t)4 * kBitmapWords * 4 : 0);
+  const bool wide = (size_t)4 * nb * sizeof(float) + own <= (size_t)max_lds_per_block();
   const int qb = wide ? 4 : 1;
   dim3 tgrid((nb + qb - 1) / qb, H);
   const size_t lds = (size_t)qb * nb * sizeof(float);
   if (TAIL) tail_vbar_kernel<D><<<dim3(w.nbp / 64 + 1, H), 256, 0, s>>>(w.vbar, w.video, w.counts,
                                                                     nb, w.nbp, w.vbt);
+  const RefQuota none{};
+  if constexpr (!TAIL) {
+    if (rq) {
+      if (wide)
+        launch_topk<D, 4, false, true>(tgrid, lds, s, w, nb, k_sel, tiles, ta, *rq);
+      else
+        launch_topk<D, 1, false, true>(tgrid, lds, s, w, nb, k_sel, tiles, ta, *rq);
+      return;
+    }
+  }
   if (wide)
-    launch_topk<D, 4, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
+    launch_topk<D, 4, TAIL, false>(tgrid, lds, s, w, nb, k_sel, tiles, ta, none);
   else
-    launch_topk<D, 1, TAIL>(tgrid, lds, s, w, nb, k_sel, tiles, ta);
+    launch_topk<D, 1, TAIL, false>(tgrid, lds, s, w, nb, k_sel, tiles, ta, none);
   if (TAIL)
     tail_v_kernel<D><<<dim3((nb + 31) / 32, H), 64 * (D / 32), 0, s>>>(w.wts, w.vbt, w.counts, nb,
                                                                       w.nbp, ta.v);
@@ -503,20 +631,22 @@ void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, in
 hipError_t launch_router(const void* q, const void* k, const void* v, bool bf16, int n, int H,
                          int D, int bs, const uint8_t* seg, int prefix, int k_sel,
                          int32_t* tiles, int32_t* prot, int prot_cap, const RouterWs& w,
-                         float scale, float* tail_lse, float* tail_v, hipStream_t s) {
+                         float scale, float* tail_lse, float* tail_v, hipStream_t s,
+                         bool guide_protected, const RefQuota* rq) {
   const int nb = (n + bs - 1) / bs;
-  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, bs, prot, prot_cap, w.video,
-                                         w.counts);
+  router_flags_kernel<<<1, 1024, 0, s>>>(seg, n, prefix, nb, bs, guide_protected, prot,
+                                         prot_cap, w.video, w.counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool tail = tail_lse != nullptr;
+  if (tail && rq) return hipErrorInvalidValue;
   const TailArgs ta{scale, n, bs, w.vbar, tail_lse, tail_v, w.wts, w.nbp};
   if (D == 128) {
-    if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
-    else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
+    if (tail) launch_pool_topk<128, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, rq, s);
+    else launch_pool_topk<128, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, rq, s);
   } else {
-    if (tail) launch_pool_topk<64, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
-    else launch_pool_topk<64, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, s);
+    if (tail) launch_pool_topk<64, true>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, rq, s);
+    else launch_pool_topk<64, false>(q, k, v, bf16, n, H, nb, bs, k_sel, tiles, w, ta, rq, s);
   }
   return hipGetLastError();
 }

@@ -128,6 +128,38 @@ int attn_router_plan(const uint8_t* seg_host, int n, int protected_prefix_len, i
                      double sparsity_ratio, int* nb, int* n_video, int* n_prot, int* k_sel);
 
 /*
+ * Reference protection ("H3 SLA Attention", inputs table, reference_protection). The
+ * guide video is the visual reference of the packed sequence; a reference tile is a
+ * video tile (see attn_router_plan) holding a guide row, and a reference range a
+ * maximal run of reference tiles with consecutive block indices.
+ *   H3_REF_OFF   no quota: reference tiles compete in the ordinary top-k.
+ *   H3_REF_LIGHT the ordinary top-k over all video tiles, plus, for each reference
+ *                range of m tiles, its best-scoring count(m, 0.85) tiles (a fixed
+ *                reference sparsity of 0.85, i.e. 15% of the range); a query block
+ *                attends the union.
+ *   H3_REF_HEAVY every reference tile is protected (attended by every query block);
+ *                the ordinary top-k runs over the other video tiles.
+ * count(m, s) is the routed-count rule of attn_router_plan. Sparsity 0 still routes
+ * every tile in every mode.
+ */
+#define H3_REF_OFF   0
+#define H3_REF_LIGHT 1
+#define H3_REF_HEAVY 2
+
+/*
+ * Router plan under a reference-protection mode (host only, no HIP call).
+ * Outputs: nb; n_video = the routed candidates (the video tiles, without the
+ * reference tiles under H3_REF_HEAVY); n_prot = the protected blocks (with the
+ * reference tiles under H3_REF_HEAVY); k_sel = the list width
+ * min(count(n_video, sparsity_ratio) + the sum of the Light quotas, n_video).
+ * Errors: as attn_router_plan, plus H3_EUNSUPPORTED for an unknown mode or, under
+ * H3_REF_LIGHT, more than 16 reference ranges.
+ */
+int attn_router_plan_ref(const uint8_t* seg_host, int n, int protected_prefix_len,
+                         int block_size, double sparsity_ratio, int reference_protection,
+                         int* nb, int* n_video, int* n_prot, int* k_sel);
+
+/*
  * Pooled block router.
  * From "H3 SLA Attention", "How it works": one product of block-mean queries
  * with block-mean keys rates all (query block, key block) pairs; each query
@@ -154,6 +186,24 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
                       const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
                       int32_t* tiles, int32_t* prot, int n_prot,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Pooled block router with reference protection (modes above). The scores, ranking,
+ * ties and outputs are those of attn_block_router; each query block's list holds the
+ * union of its selections in ascending order, padded with -1 to k_sel.
+ * seg_host: host copy of seg (the reference ranges and quotas are planned on the host).
+ * k_sel:    the list width from attn_router_plan_ref for the same arguments.
+ * n_prot:   the protected count from attn_router_plan_ref (at most that many are
+ *           written).
+ * Workspace: attn_block_router_workspace(n, heads, head_dim, block_size).
+ * Errors: as attn_block_router and attn_router_plan_ref, plus H3_EINVAL for a null
+ * seg_host or a k_sel other than the plan's width.
+ */
+int attn_block_router_ref(const void* q, const void* k, int dtype, int n, int heads,
+                          int head_dim, const uint8_t* seg, const uint8_t* seg_host,
+                          int protected_prefix_len, int block_size, double sparsity_ratio,
+                          int reference_protection, int k_sel, int32_t* tiles, int32_t* prot,
+                          int n_prot, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Block-sparse attention over routed tiles.

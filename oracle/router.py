@@ -172,7 +172,7 @@ def router_plan_ref(seg, protected_prefix_len, block_size, sparsity, mode):
     Returns (nb, protected blocks, routed-candidate video tiles, k, quotas): k is the
     ordinary top-k count over the candidates, and quotas a list of (range tiles, count)
     guaranteed per reference range (Light only). The tile-list width a query block
-    needs is k + the sum of the quota counts.
+    needs is k + the sum of the quota counts, at most the number of candidates.
     """
     nb, prot, video, k = router_plan(seg, protected_prefix_len, block_size, sparsity)
     if mode == REF_OFF:
@@ -193,10 +193,10 @@ def route_head_ref(q32_h, k32_h, seg, protected_prefix_len, block_size, sparsity
     """Routing of one head under a reference-protection mode: per query block, the
     ascending union of the ordinary top-k over the candidate video tiles and (Light)
     each reference range's quota of its best-scoring tiles, padded with -1 to the
-    list width k + sum of quotas. Returns [nqb, width] int64."""
+    list width min(k + sum of quotas, candidates). Returns [nqb, width] int64."""
     nb, _, video, k, quotas = router_plan_ref(seg, protected_prefix_len, block_size,
                                               sparsity, mode)
-    width = k + sum(c for _, c in quotas)
+    width = min(k + sum(c for _, c in quotas), len(video))
     qbar = block_means_fp32(q32_h, block_size)
     kbar = block_means_fp32(k32_h, block_size)
     chosen = [set() for _ in range(nb)]

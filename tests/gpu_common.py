@@ -80,3 +80,29 @@ def checked_routes(tiles_gpu, prot_gpu, wl, q, k, seg, k_sel, heads, bs=64, tag=
         mism = int(np.sum(np.any(got != tiles_ref, axis=2)))
         assert mism == 0, f"{tag}: {mism} tile lists differ from the oracle"
     return tiles_ref, prot_ref
+
+
+def oracle_routes_ref(wl, q, k, seg, sparsity, mode, heads, bs=64):
+    """The oracle's reference-protected routing for the given heads: (tiles
+    [len(heads), nb, width] padded with -1, protected block indices)."""
+    import oracle
+    _, prot, _, _, _ = oracle.router_plan_ref(seg, wl.protected_prefix_len, bs, sparsity, mode)
+    tiles = np.stack([oracle.route_head_ref(W.to_float32(q[:, h], wl.dtype),
+                                            W.to_float32(k[:, h], wl.dtype), seg,
+                                            wl.protected_prefix_len, bs, sparsity, mode)
+                      for h in heads])
+    return tiles, prot
+
+
+def checked_routes_ref(tiles_gpu, prot_gpu, wl, q, k, seg, sparsity, mode, heads, bs=64, tag=""):
+    """checked_routes for attn_block_router_ref: asserts the GPU lists equal the oracle's
+    bit for bit and returns the oracle's own (tiles for ``heads``, prot)."""
+    tiles_ref, prot_ref = oracle_routes_ref(wl, q, k, seg, sparsity, mode, heads, bs)
+    got_p = (prot_gpu.cpu().numpy() if prot_gpu is not None and prot_gpu.numel()
+             else np.zeros(0, dtype=np.int64))
+    assert np.array_equal(got_p, prot_ref), f"{tag}: protected list differs from the oracle"
+    got = tiles_gpu.cpu().numpy()[list(heads)]
+    assert got.shape == tiles_ref.shape, (tag, got.shape, tiles_ref.shape)
+    mism = int(np.sum(np.any(got != tiles_ref, axis=2)))
+    assert mism == 0, f"{tag}: {mism} tile lists differ from the oracle"
+    return tiles_ref, prot_ref

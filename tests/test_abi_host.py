@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     assert set(names) == set(api.EXPORTS)
     L = api.lib()
     for n in names:
@@ -95,6 +95,62 @@ def test_router_plan_errors():
         assert L.attn_router_plan(ptr, 100, 0, bs, 0.5, N0, N0, N0, N0) == api.H3_EUNSUPPORTED
     for bs in (32, 64, 128):
         assert L.attn_router_plan(ptr, 100, 0, bs, 0.5, N0, N0, N0, N0) == api.H3_OK
+
+
+def _plan_ref_oracle(seg, pre, bs, s, mode):
+    nb, prot, cand, k, quotas = oracle.router_plan_ref(seg, pre, bs, s, mode)
+    width = min(k + sum(c for _, c in quotas), len(cand))
+    return {"nb": nb, "n_video": len(cand), "n_prot": len(prot), "k_sel": width}
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_router_plan_ref_matches_oracle(mode):
+    """Reference-protection plans of the workloads and of random layouts with several
+    guide spans (reference ranges)."""
+    for wl in (W.MID_SPARSE, W.FULL_SPARSE):
+        seg, _ = W.layout(wl)
+        for bs in (32, 64, 128):
+            for s in (0.0, 0.5, 0.9, 0.999):
+                assert (api.router_plan_ref(seg, wl.protected_prefix_len, s, mode, block_size=bs)
+                        == _plan_ref_oracle(seg, wl.protected_prefix_len, bs, s, mode))
+    rng = np.random.default_rng(6)
+    for _ in range(60):
+        spans = rng.choice([0, 1, 2, 3], size=int(rng.integers(1, 12)))
+        seg = np.concatenate([np.full(int(rng.integers(1, 400)), x, dtype=np.uint8)
+                              for x in spans])
+        pre = int(rng.integers(0, len(seg) + 1))
+        s = float(rng.choice([0.0, 0.5, 0.85, 0.95]))
+        bs = int(rng.choice([32, 64, 128]))
+        want = _plan_ref_oracle(seg, pre, bs, s, mode)
+        if mode == 1 and len(oracle.reference_ranges(seg, pre, bs)) > 16:
+            continue
+        assert api.router_plan_ref(seg, pre, s, mode, block_size=bs) == want
+
+
+def test_router_ref_errors():
+    L = api.lib()
+    seg = np.array(([1] * 64 + [0] * 64) * 17, dtype=np.uint8)   # 17 reference ranges
+    ptr = seg.ctypes.data_as(ctypes.c_void_p)
+    out = [ctypes.c_int(0) for _ in range(4)]
+    refs = [ctypes.byref(x) for x in out]
+    assert L.attn_router_plan_ref(ptr, len(seg), 0, 64, 0.5, 1, *refs) == api.H3_EUNSUPPORTED
+    assert L.attn_router_plan_ref(ptr, len(seg), 0, 64, 0.5, 3, *refs) == api.H3_EUNSUPPORTED
+    assert L.attn_router_plan_ref(ptr, len(seg), 0, 64, 0.5, 2, *refs) == api.H3_OK
+    assert (out[2].value, out[1].value) == (34, 0)              # Heavy protects every block
+    seg2 = seg[:64 * 32].copy()                                  # 16 ranges: accepted
+    p2 = seg2.ctypes.data_as(ctypes.c_void_p)
+    assert L.attn_router_plan_ref(p2, len(seg2), 0, 64, 0.5, 1, *refs) == api.H3_OK
+    assert (out[1].value, out[3].value) == (16, 16)   # k = 8 + one per range, capped at 16
+    assert L.attn_router_plan_ref(None, 10, 0, 64, 0.5, 1, *refs) == api.H3_EINVAL
+    assert L.attn_router_plan_ref(p2, len(seg2), 0, 64, 1.0, 1, *refs) == api.H3_EINVAL
+    args = (P, P, 1, len(seg2), 2, 128, P)
+    # a list width other than the plan's, a missing host copy: rejected before any HIP call
+    assert L.attn_block_router_ref(*args, p2, 0, 64, 0.5, 1, 15, P, P, 16, P, BIG,
+                                   None) == api.H3_EINVAL
+    assert L.attn_block_router_ref(*args, None, 0, 64, 0.5, 1, 16, P, P, 16, P, BIG,
+                                   None) == api.H3_EINVAL
+    assert L.attn_block_router_ref(*args, p2, 0, 64, 0.5, 1, 16, P, P, 16, None, 0,
+                                   None) == api.H3_EWORKSPACE
 
 
 # ----------------------------------------------------------- argument checks
@@ -345,6 +401,9 @@ def test_forced_failure_dense(monkeypatch, env):
 def test_forced_failure_router(monkeypatch, env):
     monkeypatch.setenv("H3ATTN_FORCE_FAIL", env)
     assert router(ws=P, wsb=BIG) == api.H3_EFORCED
+    seg = np.ones(640, dtype=np.uint8)
+    assert api.lib().attn_block_router_ref(P, P, 1, 640, 2, 128, P, api._np_ptr(seg), 0, 64,
+                                           0.5, 1, 7, P, P, 0, P, BIG, None) == api.H3_EFORCED
     assert api.lib().attn_block_router_tail(P, P, P, 1, 640, 2, 128, P, 64, 64, 3, 0.088, P, P,
                                             2, P, P, P, BIG, None) == api.H3_EFORCED
 

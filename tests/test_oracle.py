@@ -492,7 +492,7 @@ def _brute_route_ref(q32, k32, seg, prefix, bs, sparsity, mode):
     groups = [(cand, count(len(cand), sparsity))]
     if mode == oracle.REF_LIGHT:
         groups += [(r, count(len(r), 0.85)) for r in ranges]
-    width = sum(c for _, c in groups)
+    width = min(sum(c for _, c in groups), len(cand))
 
     def mean(x, b):
         out = []
