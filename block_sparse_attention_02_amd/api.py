@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libh3attn.so")
 
 H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE, H3_ENOMEM = 0, -1, -2, -3, -4, -5
-H3_EFORCED = -6
+H3_EFORCED, H3_ESCRATCH = -6, -7
+H3_STATIC_SCRATCH_BYTES = 128 * 1024 * 1024
 H3_DTYPE_F32, H3_DTYPE_BF16 = 0, 1
 H3_REF_OFF, H3_REF_LIGHT, H3_REF_HEAVY = 0, 1, 2
 
@@ -26,7 +27,7 @@ EXPORTS = (
     "h3attn_version", "h3attn_status_string",
     "attn_dense_tara_workspace", "attn_dense_tara",
     "attn_router_plan", "attn_block_router_workspace", "attn_block_router",
-    "attn_router_plan_ref", "attn_block_router_ref",
+    "attn_router_plan_ref", "attn_block_router_ref", "attn_block_router_static",
     "attn_block_sparse_workspace", "attn_block_sparse",
     "attn_block_router_tail_workspace", "attn_block_router_tail", "attn_block_sparse_tail",
     "attn_block_sparse_sinks",
@@ -45,6 +46,8 @@ _SIGS = {
     "attn_router_plan": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "attn_block_router_workspace": (_sz, [_i, _i, _i, _i]),
     "attn_router_plan_ref": (_i, [_vp, _i, _i, _i, _d, _i, _vp, _vp, _vp, _vp]),
+    "attn_block_router_static": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i,
+                                      _vp]),
     "attn_block_router_ref": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _i, _d, _i, _i, _vp,
                                    _vp, _i, _vp, _sz, _vp]),
     "attn_block_router": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _i,
@@ -309,6 +312,31 @@ def attn_block_router(q, k, seg, protected_prefix_len, k_sel, n_prot, block_size
                                  _ptr(prot) if n_prot > 0 else None, n_prot,
                                  _ptr(ws), _nbytes(ws), _stream(stream))
     _check("attn_block_router", st)
+    return tiles, prot
+
+
+def attn_block_router_static(q, k, seg, protected_prefix_len, k_sel, n_prot, block_size=64,
+                             tiles=None, prot=None, stream=None):
+    """attn_block_router with the library's static device scratch instead of a workspace
+    (the library call allocates nothing; calls that overlap on one GPU race). Pass
+    preallocated ``tiles`` and ``prot`` to keep the whole call allocation-free."""
+    import torch
+    n, H, D = q.shape
+    nb = (n + block_size - 1) // block_size
+    if tiles is None:
+        tiles = torch.empty((H, nb, k_sel), dtype=torch.int32, device=q.device)
+    if prot is None:
+        prot = torch.empty((n_prot,), dtype=torch.int32, device=q.device)
+    T = _dt()
+    _check_args("attn_block_router_static", q, [
+        ("k", k, (n, H, D), (q.dtype,)), ("seg", seg, (n,), T["u8"]),
+        ("tiles", tiles, (H, nb, k_sel), T["i32"]), ("prot", prot, (n_prot,), T["i32"])])
+    st = lib().attn_block_router_static(_ptr(q), _ptr(k), _dtype_code(q), n, H, D, _ptr(seg),
+                                        protected_prefix_len, block_size, k_sel,
+                                        _ptr(tiles) if k_sel > 0 else None,
+                                        _ptr(prot) if n_prot > 0 else None, n_prot,
+                                        _stream(stream))
+    _check("attn_block_router_static", st)
     return tiles, prot
 
 

@@ -4,6 +4,7 @@
 // Every check runs before the first HIP call, so a rejected call never touches the
 // device. Kernels run on the caller's stream; nothing here synchronises.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -240,6 +241,7 @@ const char* h3attn_status_string(int status) {
     case H3_EWORKSPACE: return "workspace missing or too small";
     case H3_ENOMEM: return "host memory for the call plan could not be allocated";
     case H3_EFORCED: return "failure forced by H3ATTN_FORCE_FAIL";
+    case H3_ESCRATCH: return "problem larger than the static scratch of the call";
     default: return "unknown status";
   }
 }
@@ -406,11 +408,35 @@ size_t attn_block_router_tail_workspace(int n, int heads, int head_dim, int bloc
 
 namespace {
 
+// ------------------------------------------------------------- static scratch
+// Scratch of attn_block_router_static: a file-scope device array; every GPU the library
+// runs on holds its own copy until the process ends. In host code the array's name is
+// only a host-side handle, so host code never passes it to a kernel or a copy: it takes
+// each device's address of the array from hipGetSymbolAddress (once per device, on the
+// entry point's first call there) and passes that address.
+static __device__ __align__(256) unsigned char scratch[H3_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// This device's address of `scratch`, or null when the symbol lookup fails. Concurrent
+// first calls on one device look it up twice and store the same address.
+void* scratch_address() {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 int route(const void* q, const void* k, const void* v, int dtype, int n, int heads,
           int head_dim, const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
           int32_t* tiles, int32_t* prot, int n_prot, bool tail, float scale, float* tail_lse,
           float* tail_v, void* ws, size_t ws_bytes, void* stream,
-          bool guide_protected = false, const RefQuota* rq = nullptr) {
+          bool guide_protected = false, const RefQuota* rq = nullptr,
+          bool static_scratch = false) {
   if (!q || !k || !seg || n <= 0 || heads <= 0) return H3_EINVAL;
   if (tail && (!v || !tail_lse || !tail_v || !std::isfinite(scale) || !(scale > 0.f)))
     return H3_EINVAL;
@@ -423,8 +449,17 @@ int route(const void* q, const void* k, const void* v, int dtype, int n, int hea
   if (k_sel > nb) return H3_EINVAL;
   if (!blocks_ok(n, block_size) || nb > router_max_blocks()) return H3_EUNSUPPORTED;
   const size_t need = router_ws_bytes(n, heads, head_dim, block_size, tail);
-  if (!ws || ws_bytes < need) return H3_EWORKSPACE;
+  if (static_scratch) {
+    if (need > (size_t)H3_STATIC_SCRATCH_BYTES) return H3_ESCRATCH;
+  } else if (!ws || ws_bytes < need) {
+    return H3_EWORKSPACE;
+  }
   if (force_fail("router")) return H3_EFORCED;
+  if (static_scratch) {  // every argument check has passed: the first HIP call
+    ws = scratch_address();
+    if (!ws) return H3_ELAUNCH;
+    ws_bytes = H3_STATIC_SCRATCH_BYTES;
+  }
   RouterWs w = router_ws_carve(ws, n, heads, head_dim, block_size, tail);
   hipError_t e = launch_router(q, k, v, dtype == H3_DTYPE_BF16, n, heads, head_dim, block_size,
                                seg, protected_prefix_len, k_sel, tiles, prot, n_prot, w, scale,
@@ -493,6 +528,15 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
                       void* stream) {
   return route(q, k, nullptr, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size,
                k_sel, tiles, prot, n_prot, false, 0.f, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int attn_block_router_static(const void* q, const void* k, int dtype, int n, int heads,
+                             int head_dim, const uint8_t* seg, int protected_prefix_len,
+                             int block_size, int k_sel, int32_t* tiles, int32_t* prot,
+                             int n_prot, void* stream) {
+  return route(q, k, nullptr, dtype, n, heads, head_dim, seg, protected_prefix_len, block_size,
+               k_sel, tiles, prot, n_prot, false, 0.f, nullptr, nullptr, nullptr, 0, stream,
+               false, nullptr, true);
 }
 
 int attn_block_router_tail(const void* q, const void* k, const void* v, int dtype, int n,

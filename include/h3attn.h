@@ -52,6 +52,7 @@ extern "C" {
 #define H3_EWORKSPACE   (-4)  /* workspace pointer null or smaller than required */
 #define H3_ENOMEM       (-5)  /* host memory for a call's plan could not be allocated */
 #define H3_EFORCED      (-6)  /* failure forced by H3ATTN_FORCE_FAIL (note above) */
+#define H3_ESCRATCH     (-7)  /* larger than the static scratch of attn_block_router_static */
 
 #define H3_DTYPE_F32  0
 #define H3_DTYPE_BF16 1
@@ -186,6 +187,26 @@ int attn_block_router(const void* q, const void* k, int dtype, int n, int heads,
                       const uint8_t* seg, int protected_prefix_len, int block_size, int k_sel,
                       int32_t* tiles, int32_t* prot, int n_prot,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * attn_block_router without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Its scratch (the block means, the video-tile list and counts) lives in a
+ * static device array of H3_STATIC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the call allocates nothing. Inputs, outputs, rules and
+ * results are those of attn_block_router.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be serialised by the
+ * caller. Nothing in the array needs to start at zero.
+ * Errors: as attn_block_router without H3_EWORKSPACE, plus H3_ESCRATCH when
+ * attn_block_router_workspace(n, heads, head_dim, block_size) exceeds
+ * H3_STATIC_SCRATCH_BYTES (checked before any HIP call).
+ */
+#define H3_STATIC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int attn_block_router_static(const void* q, const void* k, int dtype, int n, int heads,
+                             int head_dim, const uint8_t* seg, int protected_prefix_len,
+                             int block_size, int k_sel, int32_t* tiles, int32_t* prot,
+                             int n_prot, void* stream);
 
 /*
  * Pooled block router with reference protection (modes above). The scores, ranking,

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert set(names) == set(api.EXPORTS)
     L = api.lib()
     for n in names:
@@ -45,7 +45,8 @@ def test_version_and_status_strings():
     assert "workspace" in api.status_string(-4)
     assert "host memory" in api.status_string(api.H3_ENOMEM)
     assert "H3ATTN_FORCE_FAIL" in api.status_string(api.H3_EFORCED)
-    assert api.status_string(-7) == "unknown status"
+    assert "static scratch" in api.status_string(api.H3_ESCRATCH)
+    assert api.status_string(-8) == "unknown status"
 
 
 def test_missing_library_fails_loudly(monkeypatch):
