@@ -15,7 +15,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libh3attn.so")
+# H3ATTN_LIB may name another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("H3ATTN_LIB") or os.path.join(_PKG, "libh3attn.so")
 
 H3_OK, H3_EINVAL, H3_EUNSUPPORTED, H3_ELAUNCH, H3_EWORKSPACE, H3_ENOMEM = 0, -1, -2, -3, -4, -5
 H3_EFORCED, H3_ESCRATCH = -6, -7
