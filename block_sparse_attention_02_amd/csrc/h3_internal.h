@@ -84,13 +84,14 @@ hipError_t launch_attn_f32(const AttnArgs& a, int D, bool sparse, bool penalty, 
 // Router.
 struct RouterWs {
   float* qbar;     // [H][nb][D]
-  float* kbar;     // [H][D][nb] (d-major)
+  float* kbar;     // [H][D][nbk] (d-major, row stride nbk = nb rounded up to 16)
   int32_t* video;  // [nb]
   int32_t* counts; // [2]: n_prot, n_video
   float* vbar;     // [H][nb][D] (tail term only, else null)
   float* wts;      // [H][nb][nbp] tail weights per (query block, video tile) (tail only)
   float* vbt;      // [H][D][nbp] V means of the video tiles, transposed (tail only)
   int nbp;         // nb rounded up to 32
+  int nbk;         // row stride of kbar
 };
 // Tail term of the unrouted tiles (see router.hip); all pointers null when not wanted.
 struct TailArgs {

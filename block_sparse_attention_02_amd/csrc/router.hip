@@ -89,78 +89,115 @@ __global__ __launch_bounds__(1024) void router_flags_kernel(const uint8_t* __res
 }
 
 // ------------------------------------------------------------------ 2. pool
-// Thread = 8 consecutive (head, d) elements of a row; workgroup = one block of bs rows.
+// Workgroup = kPoolBlocks waves, one per consecutive block of bs rows, over the same 512
+// (head, d) elements (8 per lane). Each wave adds its block's rows in row order; the
+// query (and value) means go straight to memory, row-major. The key means pass through
+// LDS so that the workgroup writes them d-major as aligned runs of kPoolBlocks floats
+// per (head, d): every store fills whole 64-byte lines (the d-major row stride is nb
+// rounded up to kPoolBlocks).
+constexpr int kPoolBlocks = 16;
+constexpr int kPoolCols = 512;   // (head, d) elements per workgroup
+constexpr int kPoolElems = 8;    // per lane
+
 template <bool BF16, int D, bool TAIL>
-__global__ __launch_bounds__(128) void router_pool_kernel(const void* __restrict__ q,
-                                                          const void* __restrict__ k,
-                                                          const void* __restrict__ v, int n,
-                                                          int H, int nb, int bs,
-                                                          float* __restrict__ qbar,
-                                                          float* __restrict__ kbar,
-                                                          float* __restrict__ vbar) {
-  const int b = blockIdx.x;
-  const int e0 = (blockIdx.y * 128 + threadIdx.x) * 8;
-  if (e0 >= H * D) return;
-  const int h = e0 / D, d0 = e0 % D;
-  const int lo = b * bs, hi = min(n, lo + bs);
-  const int64_t rs = (int64_t)H * D;
-  float aq[8], ak[8], av[8];
+__global__ __launch_bounds__(64 * kPoolBlocks) void router_pool_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int n,
+    int H, int nb, int nbk, int bs, float* __restrict__ qbar, float* __restrict__ kbar,
+    float* __restrict__ vbar) {
+  __shared__ float kt[kPoolBlocks][kPoolCols + 4];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b0 = blockIdx.x * kPoolBlocks;
+  const int b = b0 + w;
+  const int col0 = blockIdx.y * kPoolCols;
+  const int e0 = col0 + lane * kPoolElems;
+  const bool live = b < nb && e0 < H * D;
+  float ak[kPoolElems];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { aq[i] = 0.f; ak[i] = 0.f; av[i] = 0.f; }
+  for (int i = 0; i < kPoolElems; ++i) ak[i] = 0.f;
+  if (live) {
+    const int h = e0 / D, d0 = e0 % D;
+    const int lo = b * bs, hi = min(n, lo + bs);
+    const int64_t rs = (int64_t)H * D;
+    float aq[kPoolElems], av[kPoolElems];
+#pragma unroll
+    for (int i = 0; i < kPoolElems; ++i) { aq[i] = 0.f; av[i] = 0.f; }
 #pragma unroll 8
-  for (int r = lo; r < hi; ++r) {
-    const int64_t off = (int64_t)r * rs + e0;
-    float xq[8], xk[8], xv[8];
-    if (BF16) {
-      const u32x4 uq = *(const u32x4*)((const uint16_t*)q + off);
-      const u32x4 uk = *(const u32x4*)((const uint16_t*)k + off);
-      u32x4 uv = {0u, 0u, 0u, 0u};
-      if (TAIL) uv = *(const u32x4*)((const uint16_t*)v + off);
+    for (int r = lo; r < hi; ++r) {
+      const int64_t off = (int64_t)r * rs + e0;
+      float xq[8], xk[8], xv[8];
+      if (BF16) {
+        const u32x4 uq = *(const u32x4*)((const uint16_t*)q + off);
+        const u32x4 uk = *(const u32x4*)((const uint16_t*)k + off);
+        u32x4 uv = {0u, 0u, 0u, 0u};
+        if (TAIL) uv = *(const u32x4*)((const uint16_t*)v + off);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xq[2 * i] = __uint_as_float(uq[i] << 16);
-        xq[2 * i + 1] = __uint_as_float(uq[i] & 0xFFFF0000u);
-        xk[2 * i] = __uint_as_float(uk[i] << 16);
-        xk[2 * i + 1] = __uint_as_float(uk[i] & 0xFFFF0000u);
-        xv[2 * i] = __uint_as_float(uv[i] << 16);
-        xv[2 * i + 1] = __uint_as_float(uv[i] & 0xFFFF0000u);
-      }
-    } else {
-      const f32x4* pq = (const f32x4*)((const float*)q + off);
-      const f32x4* pk = (const f32x4*)((const float*)k + off);
-      const f32x4 q0 = pq[0], q1 = pq[1], k0 = pk[0], k1 = pk[1];
-      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
-      if (TAIL) {
-        const f32x4* pv = (const f32x4*)((const float*)v + off);
-        v0 = pv[0];
-        v1 = pv[1];
+        for (int i = 0; i < 4; ++i) {
+          xq[2 * i] = __uint_as_float(uq[i] << 16);
+          xq[2 * i + 1] = __uint_as_float(uq[i] & 0xFFFF0000u);
+          xk[2 * i] = __uint_as_float(uk[i] << 16);
+          xk[2 * i + 1] = __uint_as_float(uk[i] & 0xFFFF0000u);
+          xv[2 * i] = __uint_as_float(uv[i] << 16);
+          xv[2 * i + 1] = __uint_as_float(uv[i] & 0xFFFF0000u);
+        }
+      } else {
+        const f32x4* pq = (const f32x4*)((const float*)q + off);
+        const f32x4* pk = (const f32x4*)((const float*)k + off);
+        const f32x4 q0 = pq[0], q1 = pq[1], k0 = pk[0], k1 = pk[1];
+        f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (TAIL) {
+          const f32x4* pv = (const f32x4*)((const float*)v + off);
+          v0 = pv[0];
+          v1 = pv[1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xq[i] = q0[i]; xq[4 + i] = q1[i];
+          xk[i] = k0[i]; xk[4 + i] = k1[i];
+          xv[i] = v0[i]; xv[4 + i] = v1[i];
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xq[i] = q0[i]; xq[4 + i] = q1[i];
-        xk[i] = k0[i]; xk[4 + i] = k1[i];
-        xv[i] = v0[i]; xv[4 + i] = v1[i];
+      for (int i = 0; i < 8; ++i) {
+        aq[i] = __fadd_rn(aq[i], xq[i]);
+        ak[i] = __fadd_rn(ak[i], xk[i]);
+        if (TAIL) av[i] = __fadd_rn(av[i], xv[i]);
       }
     }
+    const float cnt = (float)(hi - lo);
+    f32x4 m0, m1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      aq[i] = __fadd_rn(aq[i], xq[i]);
-      ak[i] = __fadd_rn(ak[i], xk[i]);
-      if (TAIL) av[i] = __fadd_rn(av[i], xv[i]);
+    for (int i = 0; i < 4; ++i) {
+      m0[i] = __fdiv_rn(aq[i], cnt);
+      m1[i] = __fdiv_rn(aq[4 + i], cnt);
     }
-  }
-  const float cnt = (float)(hi - lo);
-  float* oq = qbar + ((int64_t)h * nb + b) * D + d0;   // [H][nb][D]
-  float* ok = kbar + ((int64_t)h * D + d0) * nb + b;   // [H][D][nb]
+    float* oq = qbar + ((int64_t)h * nb + b) * D + d0;   // [H][nb][D]
+    *(f32x4*)oq = m0;
+    *(f32x4*)(oq + 4) = m1;
+    if (TAIL) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    oq[i] = __fdiv_rn(aq[i], cnt);
-    ok[(int64_t)i * nb] = __fdiv_rn(ak[i], cnt);
-  }
-  if (TAIL) {
-    float* ov = vbar + ((int64_t)h * nb + b) * D + d0;  // [H][nb][D]
+      for (int i = 0; i < 4; ++i) {
+        m0[i] = __fdiv_rn(av[i], cnt);
+        m1[i] = __fdiv_rn(av[4 + i], cnt);
+      }
+      float* ov = vbar + ((int64_t)h * nb + b) * D + d0;  // [H][nb][D]
+      *(f32x4*)ov = m0;
+      *(f32x4*)(ov + 4) = m1;
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ov[i] = __fdiv_rn(av[i], cnt);
+    for (int i = 0; i < 8; ++i) ak[i] = __fdiv_rn(ak[i], cnt);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kt[w][lane * kPoolElems + i] = ak[i];  // zero past the end
+  __syncthreads();
+  // [H][D][nbk]: thread t stores blocks 4p..4p+3 (p = t % 4) of column t / 4, so four
+  // neighbouring threads fill one 64-byte run
+  for (int idx = threadIdx.x; idx < kPoolCols * 4; idx += 64 * kPoolBlocks) {
+    const int c = idx >> 2, p4 = (idx & 3) * 4;
+    const int e = col0 + c;
+    if (e >= H * D) continue;
+    const int h = e / D, d = e % D;
+    *(f32x4*)(kbar + ((int64_t)h * D + d) * nbk + b0 + p4) =
+        f32x4{kt[p4][c], kt[p4 + 1][c], kt[p4 + 2][c], kt[p4 + 3][c]};
   }
 }
 
@@ -188,7 +225,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           const float* __restrict__ kbar,
                                                           const int32_t* __restrict__ video,
                                                           const int32_t* __restrict__ counts,
-                                                          int nb, int k_sel,
+                                                          int nb, int nbk, int k_sel,
                                                           int32_t* __restrict__ tiles,
                                                           TailArgs tail, RefQuota rq) {
   static_assert(QB == 1 || QB == 4, "query blocks per workgroup");
@@ -211,8 +248,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 #pragma unroll
   for (int j = 0; j < QB; ++j) qrow[j] = qbar + ((int64_t)h * nb + min(qb0 + j, nb - 1)) * D;
   // Lanes take consecutive video tiles, so each d reads one coalesced run of the
-  // d-major kbar.
-  const float* kh = kbar + (int64_t)h * D * nb;
+  // d-major kbar (row stride nbk).
+  const float* kh = kbar + (int64_t)h * D * nbk;
   for (int vi = tid; vi < nv; vi += 256) {
     const int kb = video[vi];
     float acc[QB];
@@ -220,7 +257,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     for (int j = 0; j < QB; ++j) acc[j] = 0.f;
 #pragma unroll 8
     for (int d = 0; d < D; ++d) {
-      const float kv = kh[(int64_t)d * nb + kb];
+      const float kv = kh[(int64_t)d * nbk + kb];
 #pragma unroll
       for (int j = 0; j < QB; ++j) acc[j] = acc[j] + mul_rounded(qrow[j][d], kv);
     }
@@ -521,11 +558,15 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
+// Row stride of the d-major key means: the block count rounded up to whole pool groups.
+inline size_t kbar_stride(size_t nb) { return (nb + kPoolBlocks - 1) / kPoolBlocks * kPoolBlocks; }
+
 size_t router_ws_bytes(int n, int H, int D, int bs, bool tail) {
   const size_t nb = (size_t)((n + bs - 1) / bs);
   const size_t nbp = (nb + 31) / 32 * 32;
   const size_t means = align256(nb * H * D * sizeof(float));
-  size_t b = 2 * means + align256(nb * sizeof(int32_t)) + 256;
+  const size_t kmeans = align256(kbar_stride(nb) * H * D * sizeof(float));
+  size_t b = means + kmeans + align256(nb * sizeof(int32_t)) + 256;
   if (tail)
     b += means + align256((size_t)H * nb * nbp * 4) + align256((size_t)H * D * nbp * 4);
   return b;
@@ -539,7 +580,8 @@ RouterWs router_ws_carve(void* ws, int n, int H, int D, int bs, bool tail) {
   w.qbar = (float*)p;
   p += means;
   w.kbar = (float*)p;
-  p += means;
+  w.nbk = (int)kbar_stride(nb);
+  p += align256((size_t)w.nbk * H * D * sizeof(float));
   w.video = (int32_t*)p;
   p += align256(nb * sizeof(int32_t));
   w.counts = (int32_t*)p;
@@ -585,21 +627,21 @@ template <int D, int QB, bool TAIL, bool REF>
 void launch_topk(dim3 grid, size_t lds, hipStream_t s, const RouterWs& w, int nb, int k_sel,
                  int32_t* tiles, const TailArgs& ta, const RefQuota& rq) {
   router_topk_kernel<D, QB, TAIL, REF><<<grid, 256, lds, s>>>(w.qbar, w.kbar, w.video, w.counts,
-                                                              nb, k_sel, tiles, ta, rq);
+                                                              nb, w.nbk, k_sel, tiles, ta, rq);
 }
 
 template <int D, bool TAIL>
 void launch_pool_topk(const void* q, const void* k, const void* v, bool bf16, int n, int H,
                       int nb, int bs, int k_sel, int32_t* tiles, const RouterWs& w,
                       const TailArgs& ta, const RefQuota* rq, hipStream_t s) {
-  const int chunks = (H * D / 8 + 127) / 128;
-  dim3 pgrid(nb, chunks);
+  const int chunks = (H * D + kPoolCols - 1) / kPoolCols;
+  dim3 pgrid((nb + kPoolBlocks - 1) / kPoolBlocks, chunks);
   if (bf16)
-    router_pool_kernel<true, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, bs, w.qbar,
-                                                             w.kbar, w.vbar);
+    router_pool_kernel<true, D, TAIL><<<pgrid, 64 * kPoolBlocks, 0, s>>>(
+        q, k, v, n, H, nb, w.nbk, bs, w.qbar, w.kbar, w.vbar);
   else
-    router_pool_kernel<false, D, TAIL><<<pgrid, 128, 0, s>>>(q, k, v, n, H, nb, bs, w.qbar,
-                                                              w.kbar, w.vbar);
+    router_pool_kernel<false, D, TAIL><<<pgrid, 64 * kPoolBlocks, 0, s>>>(
+        q, k, v, n, H, nb, w.nbk, bs, w.qbar, w.kbar, w.vbar);
   // four query blocks per workgroup when their scores fit in the LDS next to the
   // kernel's own arrays (about 12 KB, and 4 bitmaps of the reference quota)
   const size_t own = 12 * 1024 + (rq ? (size_t)4 * kBitmapWords * 4 : 0);

@@ -198,9 +198,11 @@ def test_workspace_sizes():
     assert L.attn_block_sparse_workspace(129, 2, 64, 1) == _a256(2 * 64 * 192 * 2) + _a256(3 * 16)
     for bs in (32, 64, 128):
         nb = (31552 + bs - 1) // bs
-        # two float32 means per (head, block, d), the video-block list and the counts
+        nbk = (nb + 15) // 16 * 16
+        # float32 query and key means per (head, block, d) (the d-major key means with rows
+        # of nb rounded up to 16), the video-block list and the counts
         assert (L.attn_block_router_workspace(31552, 24, 128, bs)
-                == 2 * _a256(nb * 24 * 128 * 4) + _a256(nb * 4) + 256)
+                == _a256(nb * 24 * 128 * 4) + _a256(nbk * 24 * 128 * 4) + _a256(nb * 4) + 256)
     assert L.attn_block_router_workspace(31552, 24, 128, 16) == 0
 
 
