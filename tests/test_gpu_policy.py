@@ -79,3 +79,54 @@ def test_policy_dense_failure_is_reported(case, monkeypatch):
     with pytest.raises(api.H3Error) as e:
         _run(case, policy.SparsePolicy(0.8, 64, 100, min_seq_len=1000))
     assert e.value.status == api.H3_EFORCED and e.value.func == "attn_dense_tara"
+
+
+@pytest.mark.parametrize("kw,mode", [
+    (dict(reference_protection="light"), "light"),
+    (dict(reference_protection="heavy"), "heavy"),
+    (dict(tail_correction=True), None),
+    (dict(sink_segments=(W.SEG_AUDIO,)), None),
+    (dict(use_int8_qk=True), None),
+    (dict(use_int8_qk=True, tail_correction=True, sink_segments=(W.SEG_AUDIO,)), None),
+])
+def test_policy_knobs_match_oracle(case, monkeypatch, kw, mode):
+    """Each path-selecting input of the node's table ("H3 SLA Attention", inputs table):
+    the policy's routed result equals the oracle's block-sparse result over the oracle's
+    own lists, with the same quota, tail terms, sink blocks or int8 scores."""
+    from test_gpu_small import _tails_oracle
+    from gpu_common import oracle_routes_ref
+    monkeypatch.delenv("H3ATTN_FORCE_FAIL", raising=False)
+    wl, seg, t, seg_d, t_d, raw, dev, host, dense_ref = case
+    pol = policy.SparsePolicy(0.8, 64, 100, min_seq_len=1000, **kw)
+    print(f"case policy knobs {kw}", flush=True)
+    o, lse, path = _run(case, pol)
+    assert path == "block_sparse"
+    if mode:
+        from oracle.router import REF_HEAVY, REF_LIGHT
+        code = {"light": REF_LIGHT, "heavy": REF_HEAVY}[mode]
+        tiles, prot = oracle_routes_ref(wl, raw[0], raw[1], seg, 0.8, code, range(2))
+    else:
+        plan = api.router_plan(seg, 100, 0.8)
+        tiles, prot = oracle_routes(wl, raw[0], raw[1], seg, plan["k_sel"], range(2))
+    tails = (_tails_oracle(wl, *raw, seg, tiles, range(2))
+             if kw.get("tail_correction") else None)
+    ref = oracle.block_sparse(*host, seg, t, wl.tara, wl.scale, 64, prot, tiles, tails=tails,
+                              sink_segments=kw.get("sink_segments", ()),
+                              int8_qk=kw.get("use_int8_qk", False))
+    o_ref = np.zeros((wl.n, 2, 128))
+    l_ref = np.zeros((wl.n, 2))
+    for (h, qb), (ob, lb) in ref.items():
+        o_ref[qb * 64:qb * 64 + len(ob), h] = ob
+        l_ref[qb * 64:qb * 64 + len(ob), h] = lb
+    compare(o, lse, o_ref, l_ref, "bf16", f"policy {kw}")
+
+
+def test_policy_dense_step_matches_dense_oracle(case, monkeypatch):
+    monkeypatch.delenv("H3ATTN_FORCE_FAIL", raising=False)
+    wl, seg, t, seg_d, t_d, raw, dev, host, dense_ref = case
+    pol = policy.SparsePolicy(0.8, 64, 100, min_seq_len=1000, dense_last_steps=1)
+    o, lse, path = policy.attention(*dev, seg_d, t_d, seg, pol, *wl.tara, scale=wl.scale,
+                                    step=5, total_steps=6)
+    torch.cuda.synchronize()
+    assert path == "dense"
+    compare(o, lse, *dense_ref, "bf16", "policy dense last step")

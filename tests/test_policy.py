@@ -64,6 +64,59 @@ class HookedOps:
             raise api.H3Error("attn_block_sparse", st)
         return "sparse_o", "sparse_lse"
 
+    router_plan_ref = staticmethod(api.router_plan_ref)
+
+    def attn_block_router_ref(self, q, k, seg, seg_host, prefix, sparsity, mode, block_size=64):
+        self.calls.append("router_ref")
+        if not _forced("router"):
+            return "tiles", "prot"
+        n, H, D = q.shape
+        plan = api.router_plan_ref(seg_host, prefix, sparsity, mode, block_size)
+        seg_host = np.ascontiguousarray(seg_host, dtype=np.uint8)
+        st = api.lib().attn_block_router_ref(P, P, 1, n, H, D, P, seg_host.ctypes.data, prefix,
+                                             block_size, sparsity, mode, plan["k_sel"], P, P,
+                                             plan["n_prot"], P, BIG, None)
+        if st:
+            raise api.H3Error("attn_block_router_ref", st)
+        return "tiles", "prot"
+
+    def attn_block_router_tail(self, q, k, v, seg, prefix, k_sel, n_prot, scale=None,
+                               block_size=64):
+        self.calls.append("router_tail")
+        if not _forced("router"):
+            return "tiles", "prot", "tail_lse", "tail_v"
+        n, H, D = q.shape
+        st = api.lib().attn_block_router_tail(P, P, P, 1, n, H, D, P, prefix, block_size, k_sel,
+                                              0.088, P, P, n_prot, P, P, P, BIG, None)
+        if st:
+            raise api.H3Error("attn_block_router_tail", st)
+        return "tiles", "prot", "tail_lse", "tail_v"
+
+    def _sparse_variant(self, name, q, tara, sinks, tail, block_size):
+        self.calls.append(name)
+        if not _forced("sparse"):
+            return name + "_o", name + "_lse"
+        n, H, D = q.shape
+        fn = "attn_block_sparse_" + ("int8qk" if name == "sparse_int8" else "sinks")
+        tl = P if tail else None
+        st = getattr(api.lib(), fn)(P, P, P, 1, n, H, D, P, P, *tara, 0.088, block_size, P, 1,
+                                    P, 1, tl, tl, sinks, P, 1, P, P, BIG, None)
+        if st:
+            raise api.H3Error(fn, st)
+        return name + "_o", name + "_lse"
+
+    def attn_block_sparse_sinks(self, q, k, v, seg, t, tiles, prot, sinks, tail_lse, tail_v,
+                                *tara, scale=None, block_size=64, o=None, lse=None):
+        self.args = (sinks, tail_lse, tail_v)
+        return self._sparse_variant("sparse_sinks", q, tara, sinks, tail_lse is not None,
+                                    block_size)
+
+    def attn_block_sparse_int8qk(self, q, k, v, seg, t, tiles, prot, tail_lse, tail_v, sinks,
+                                 *tara, scale=None, block_size=64, o=None, lse=None):
+        self.args = (sinks, tail_lse, tail_v)
+        return self._sparse_variant("sparse_int8", q, tara, sinks, tail_lse is not None,
+                                    block_size)
+
     def attn_dense_tara(self, *args, **kw):
         self.calls.append("dense")
         return "dense_o", "dense_lse"
@@ -119,3 +172,107 @@ def test_short_or_unsparsified_sequences_stay_dense(caplog, n, sparsity, expect)
 
 def test_min_seq_len_default_is_the_inputs_table_value():
     assert policy.SparsePolicy().min_seq_len == 12228
+
+
+def _pol(**kw):
+    wl = W.FULL_SPARSE
+    return policy.SparsePolicy(0.9, 64, wl.protected_prefix_len, **kw)
+
+
+@pytest.mark.parametrize("kw,calls,tag", [
+    (dict(reference_protection="Light"), ["router_ref", "sparse"], "reference light"),
+    (dict(reference_protection="Heavy Enforcement"), ["router_ref", "sparse"], "reference heavy"),
+    (dict(tail_correction=True), ["router_tail", "sparse_sinks"], "tail"),
+    (dict(use_int8_qk=True), ["router", "sparse_int8"], "int8 QK"),
+    (dict(use_int8_qk=True, tail_correction=True), ["router_tail", "sparse_int8"], "tail"),
+    (dict(sink_segments=(W.SEG_AUDIO,)), ["router", "sparse_sinks"], "sinks [2]"),
+])
+def test_policy_knobs_pick_the_entry_points(monkeypatch, caplog, kw, calls, tag):
+    """Each path-selecting input of the node's table routes to its library calls, and the
+    log line names it."""
+    monkeypatch.delenv("H3ATTN_FORCE_FAIL", raising=False)
+    wl, q, seg = _case()
+    ops = HookedOps()
+    with caplog.at_level(logging.INFO, logger="h3attn"):
+        o, lse, path = policy.attention(q, q, q, None, None, seg, _pol(**kw), ops=ops)
+    assert path == "block_sparse" and ops.calls == calls and tag in caplog.text
+    if "sparse_sinks" in calls or "sparse_int8" in calls:
+        sinks, tl, tv = ops.args
+        assert sinks == sum(1 << s for s in kw.get("sink_segments", ()))
+        assert (tl == "tail_lse") == bool(kw.get("tail_correction"))
+
+
+def test_reference_protection_plans_the_list_width(monkeypatch, caplog):
+    monkeypatch.delenv("H3ATTN_FORCE_FAIL", raising=False)
+    wl, q, seg = _case()
+    with caplog.at_level(logging.INFO, logger="h3attn"):
+        policy.attention(q, q, q, None, None, seg, _pol(reference_protection="light"),
+                         ops=HookedOps())
+    plan = api.router_plan_ref(seg, wl.protected_prefix_len, 0.9, api.H3_REF_LIGHT)
+    assert f"{plan['n_prot']} protected + {plan['k_sel']} routed" in caplog.text
+
+
+@pytest.mark.parametrize("kw,family,func", [
+    (dict(reference_protection="light"), "router", "attn_block_router_ref"),
+    (dict(reference_protection="heavy"), "router", "attn_block_router_ref"),
+    (dict(tail_correction=True), "router", "attn_block_router_tail"),
+    (dict(tail_correction=True), "sparse", "attn_block_sparse_sinks"),
+    (dict(sink_segments=(W.SEG_AUDIO,)), "sparse", "attn_block_sparse_sinks"),
+    (dict(use_int8_qk=True), "sparse", "attn_block_sparse_int8qk"),
+])
+def test_variant_failures_fall_back_to_dense(monkeypatch, caplog, kw, family, func):
+    """The variant entry points answer the library hook like the plain ones, and the policy
+    falls back to dense TARA naming the entry point that failed."""
+    monkeypatch.setenv("H3ATTN_FORCE_FAIL", family)
+    wl, q, seg = _case()
+    ops = HookedOps()
+    with caplog.at_level(logging.INFO, logger="h3attn"):
+        o, lse, path = policy.attention(q, q, q, None, None, seg, _pol(**kw), ops=ops)
+    assert path == "dense_fallback" and o == "dense_o" and ops.calls[-1] == "dense"
+    assert f"{func} returned status {api.H3_EFORCED}" in caplog.text
+
+
+def test_disabled_policy_runs_dense(caplog):
+    wl, q, seg = _case()
+    ops = HookedOps()
+    with caplog.at_level(logging.INFO, logger="h3attn"):
+        o, lse, path = policy.attention(q, q, q, None, None, seg, _pol(enabled=False), ops=ops)
+    assert path == "dense" and ops.calls == ["dense"] and "(disabled)" in caplog.text
+
+
+@pytest.mark.parametrize("step,total,expect", [(None, None, "block_sparse"), (0, 8, "dense"),
+                                                (2, 8, "dense"), (3, 8, "block_sparse"),
+                                                (6, 8, "block_sparse"), (7, 8, "dense"),
+                                                (7, None, "block_sparse")])
+def test_dense_steps_and_dense_last_steps(monkeypatch, step, total, expect):
+    """dense_steps '0-2' and dense_last_steps 1 over an 8-step run: steps 0, 1, 2 and 7 run
+    dense; without a step index the policy cannot tell and routes."""
+    monkeypatch.delenv("H3ATTN_FORCE_FAIL", raising=False)
+    wl, q, seg = _case()
+    ops = HookedOps()
+    pol = _pol(dense_steps="0-2", dense_last_steps=1)
+    _, _, path = policy.attention(q, q, q, None, None, seg, pol, step=step, total_steps=total,
+                                  ops=ops)
+    assert path == expect
+
+
+def test_parse_steps():
+    assert policy.parse_steps("") == frozenset()
+    assert policy.parse_steps("0,1") == {0, 1}
+    assert policy.parse_steps("0-2, 5") == {0, 1, 2, 5}
+    assert policy.parse_steps([3, 4]) == {3, 4}
+    for bad in ("2-1", "-1", "a"):
+        with pytest.raises(ValueError):
+            policy.parse_steps(bad)
+
+
+@pytest.mark.parametrize("kw", [dict(reference_protection="medium"),
+                                dict(reference_protection="light", tail_correction=True),
+                                dict(use_int8_qk=True, block_size=32), dict(block_size=96),
+                                dict(sparsity_ratio=1.0), dict(dense_last_steps=-1),
+                                dict(sink_segments=(9,))])
+def test_unsupported_knob_combinations_are_rejected(kw):
+    base = dict(sparsity_ratio=0.9, block_size=64)
+    base.update(kw)
+    with pytest.raises(ValueError):
+        policy.SparsePolicy(**base)
