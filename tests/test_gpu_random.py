@@ -13,6 +13,8 @@ protected prefix, then checks against the float64 oracle:
 A second set of cases takes the knobs to their extremes (protected prefixes 0 and n,
 sparsity 0.99, strength up to 50 and cap up to 60, falloff 0.01, a second softmax scale)
 and also feeds hand-built tile lists with repeated, negative and out-of-range entries.
+A third set draws layouts with several guide-video spans and checks the reference-
+protection router (Light / Heavy) and the attention over its lists.
 The seeds are fixed, so every run draws the same cases."""
 import numpy as np
 import pytest
@@ -93,12 +95,12 @@ def test_random_layouts(seed):
     o, lse = api.attn_block_sparse_sinks(qd, kd, vd, seg_d, t_d, tiles, prot, sinks, tl, tv,
                                          *wl.tara, scale=wl.scale, block_size=bs)
     torch.cuda.synchronize()
-    tiles_np = tiles.cpu().numpy()
+    tiles_ref = _route_oracle(wl, q, k, seg, plan["k_sel"], range(H), bs=bs)
     assert np.array_equal(prot.cpu().numpy(), prot_ref)
-    assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(H), bs=bs))
-    tails = _tails_oracle(wl, q, k, v, seg, tiles_np, range(H), bs=bs) if sp["tail"] else None
+    assert np.array_equal(tiles.cpu().numpy(), tiles_ref)
+    tails = _tails_oracle(wl, q, k, v, seg, tiles_ref, range(H), bs=bs) if sp["tail"] else None
     sink_segs = (W.SEG_AUDIO,) if sp["sinks"] else ()
-    ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, bs, prot_ref, tiles_np,
+    ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, bs, prot_ref, tiles_ref,
                               tails=tails, sink_segments=sink_segs)
     o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
     compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} sparse")
@@ -112,7 +114,7 @@ def test_random_layouts(seed):
                                               block_size=bs)
         torch.cuda.synchronize()
         ref = oracle.block_sparse(q64, k64, v64, seg, t, wl.tara, wl.scale, bs, prot_ref,
-                                  tiles_np, tails=tails, sink_segments=sink_segs, int8_qk=True)
+                                  tiles_ref, tails=tails, sink_segments=sink_segs, int8_qk=True)
         o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
         compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} int8")
 
@@ -178,11 +180,11 @@ def test_random_extremes(seed):
             tiles, prot = api.attn_block_router(qd, kd, seg_d, prefix, plan["k_sel"],
                                                 plan["n_prot"], block_size=bs)
         torch.cuda.synchronize()
-        tiles_np, prot_np = tiles.cpu().numpy(), prot.cpu().numpy()
-        _, prot_ref, _, _ = oracle.router_plan(seg, prefix, bs, sp["sparsity"])
-        assert np.array_equal(prot_np, prot_ref)
-        assert np.array_equal(tiles_np, _route_oracle(wl, q, k, seg, plan["k_sel"], range(H),
-                                                       bs=bs))
+        _, prot_np, _, _ = oracle.router_plan(seg, prefix, bs, sp["sparsity"])
+        tiles_np = _route_oracle(wl, q, k, seg, plan["k_sel"], range(H), bs=bs)
+        # the GPU lists must equal the oracle's; the oracle then runs on its own lists
+        assert np.array_equal(prot.cpu().numpy(), prot_np)
+        assert np.array_equal(tiles.cpu().numpy(), tiles_np)
         if sp["tail"]:
             tails = {h: oracle.tail_terms(W.to_float32(q[:, h], dtype), W.to_float32(k[:, h], dtype),
                                           v64[:, h], seg, prefix, bs, tiles_np[h], scale)
@@ -201,3 +203,55 @@ def test_random_extremes(seed):
         l_ref = np.where(empty, 0.0, l_ref)
         lse = torch.where(torch.isneginf(lse), torch.zeros_like(lse), lse)
     compare(o, lse, o_ref, l_ref, dtype, f"{wl.name} sparse")
+
+
+def _reference_case(seed):
+    """A packed layout with one to three guide-video spans apart from each other (each one
+    or more reference ranges), a protected prefix, and a random reference mode."""
+    rng = np.random.default_rng(11000 + seed)
+    n_guides = int(rng.integers(1, 4))
+    spans = [W.Span(W.SEG_TEXT, int(rng.integers(1, 150)))]
+    for g in range(n_guides):
+        frames = int(rng.integers(1, 6))
+        spans.append(W.Span(W.SEG_GUIDE, frames * int(rng.integers(20, 220)), frames))
+        spans.append(W.Span(int(rng.choice([W.SEG_AUDIO, W.SEG_OUTPUT, W.SEG_TEXT])),
+                            int(rng.integers(1, 300))))
+    frames = int(rng.integers(1, 6))
+    spans.append(W.Span(W.SEG_OUTPUT, frames * int(rng.integers(40, 300)), frames))
+    wl = W.custom(f"reference_{seed}", spans, heads=int(rng.integers(1, 4)),
+                  head_dim=int(rng.choice([64, 128])), dtype="bf16", seed_index=500 + seed,
+                  frame_weight=float(rng.choice([0.0, 0.7])),
+                  protected_prefix_len=int(rng.integers(0, spans[0].length + 1)))
+    return wl, dict(bs=int(rng.choice([32, 64, 128])),
+                    sparsity=float(rng.choice([0.0, 0.5, 0.85, 0.95])),
+                    mode=int(rng.choice([api.H3_REF_LIGHT, api.H3_REF_HEAVY])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_reference_protection(seed):
+    """Reference protection ("H3 SLA Attention", inputs table) on random layouts with
+    several guide spans: the quota router's lists and protected list bit-exact against the
+    oracle, then block-sparse attention over the oracle's lists, every output row."""
+    from gpu_common import checked_routes_ref
+    from oracle.router import REF_HEAVY, REF_LIGHT
+    wl, sp = _reference_case(seed)
+    H, d, bs = wl.heads, wl.head_dim, sp["bs"]
+    seg, t, seg_d, t_d = layout_device(wl)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    print(f"case {wl.name} n={wl.n} spans={[(s.seg, s.length, s.frames) for s in wl.spans]} "
+          f"H={H} d={d} prefix={wl.protected_prefix_len} {sp}", flush=True)
+    tiles, prot = api.attn_block_router_ref(qd, kd, seg_d, seg, wl.protected_prefix_len,
+                                            sp["sparsity"], sp["mode"], block_size=bs)
+    torch.cuda.synchronize()
+    mode = REF_LIGHT if sp["mode"] == api.H3_REF_LIGHT else REF_HEAVY
+    tiles_ref, prot_ref = checked_routes_ref(tiles, prot, wl, q, k, seg, sp["sparsity"], mode,
+                                             range(H), bs=bs, tag=wl.name)
+    o, lse = api.attn_block_sparse(qd, kd, vd, seg_d, t_d, tiles if tiles.shape[-1] else None,
+                                   prot if prot.numel() else None, *wl.tara, scale=wl.scale,
+                                   block_size=bs)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
+                              wl.scale, bs, prot_ref, tiles_ref)
+    o_ref, l_ref = _assemble(ref, wl.n, H, d, bs)
+    compare(o, lse, o_ref, l_ref, "bf16", f"{wl.name} reference sparse")
