@@ -54,9 +54,11 @@ def test_router_and_sparse_at_block_limit():
     got_tiles = tiles[0].cpu().numpy()
     assert np.array_equal(got_tiles[blocks], ref_tiles)
 
+    # the oracle attends over its own lists of the sampled blocks
+    tl_ref = np.full((1, nb, k_sel), -1, dtype=np.int64)
+    tl_ref[0, blocks] = ref_tiles
     ref = oracle.block_sparse(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), seg, t, wl.tara,
-                              wl.scale, 64, prot_ref, got_tiles[None], heads=[0],
-                              qblocks=blocks)
+                              wl.scale, 64, prot_ref, tl_ref, heads=[0], qblocks=blocks)
     og, lg, orf, lrf = [], [], [], []
     for (_, qb), (ob, lb) in ref.items():
         lo, hi = qb * 64, min(wl.n, qb * 64 + 64)
